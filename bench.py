@@ -1,0 +1,283 @@
+"""Benchmark: one KIVI int4 decode step on one MI355X.
+
+A step is the decode hot path over one batch: append one new fp16 K/V token
+per request (Value eviction and quantisation, Key flush when a residual
+fills, residual write) and then split-K paged decode attention over the
+quantised cache plus residual, with the cross-split merge.
+
+Workload: Llama-3-8B-shaped decode layer, 32 requests x 4096 cached tokens,
+32 query / 8 KV heads, head_dim 128, int4 (Key per-channel G=64, Value
+per-token Gv=128), residual R=128, 16-token pages. Inputs are seeded
+synthetic data. To keep the 256 MB last-level cache from serving the
+~153 MB working set, steps rotate over replica caches (>= 512 MB in total).
+
+Prints one JSON line. `value` is algorithmic HBM GB/s of the attention
+(codes + group metadata once + residual + q/out + page table) per whole step;
+`roofline` relates the same bytes to the decode call's own duration, timed
+with HIP events on the stream it was launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 or 3)")
+    ap.add_argument("--bits", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="0 = size for ~10-30 s")
+    return ap.parse_args()
+
+
+def decode_bytes(lens, w) -> int:
+    """Algorithmic bytes one decode call must move (metadata counted once per group)."""
+    d, es = 128, 2
+    b = w.bits
+    G, Gv, R = w.k_group, w.v_group, w.residual
+    g = w.num_q_heads // w.num_kv_heads
+    total = 0
+    for T in lens:
+        T = int(T)
+        TK = R * (T // R)
+        TV = max(0, T - R)
+        per_head = (TK * d * b // 8 + (TK // G) * d * 4 + TV * d * b // 8 + TV * (d // Gv) * 4
+                    + (T - TK) * d * es + (T - TV) * d * es + 2 * g * d * es)
+        total += per_head * w.num_kv_heads + 4 * math.ceil(T / w.block_size)
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kivi_quantized_kv_append_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_name: str):
+    """HBM bytes per decode launch from committed rocprofv3 PMC summaries, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.txt" % cfg_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU part. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from kivi_quantized_kv_append_amd import inputs, kivi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kivi.load()
+
+    n_steps, n_warm = args.steps, args.warmup
+    w0 = inputs.config(args.config, bits=args.bits)
+    S, H, HQ, d = w0.num_seqs, w0.num_kv_heads, w0.num_q_heads, 128
+    T0 = int(w0.seq_lens[0])
+    base_bytes = decode_bytes(w0.seq_lens, w0)
+    n_rep = max(1, math.ceil(2 * MALL_BYTES / base_bytes))
+    steps_per_rep = math.ceil((n_warm + n_steps) / n_rep)
+    w = inputs.config(args.config, bits=args.bits, extra_tokens=steps_per_rep + 1)
+    scale = 1.0 / math.sqrt(d)
+
+    # ---- inputs (seeded) ----
+    t_gen = time.perf_counter()
+    streams = [w.kv_stream(s) for s in range(S)]
+    k_init = np.stack([streams[s][0][:T0] for s in range(S)])  # [S][T0][H][d]
+    v_init = np.stack([streams[s][1][:T0] for s in range(S)])
+    gen_s = time.perf_counter() - t_gen
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, w.num_blocks,
+                           S, w.dtype)
+    pool_bytes = kivi.kivi_cache_pool_bytes(cfg)
+    bt_np = w.block_table()
+    bt = torch.from_numpy(bt_np).to(dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    cu_init = torch.arange(0, (S + 1) * T0, T0, dtype=torch.int32, device=dev)
+    cu_one = torch.arange(0, S + 1, dtype=torch.int32, device=dev)
+    dk = dev_u16(k_init.reshape(S * T0, H, d))
+    dv = dev_u16(v_init.reshape(S * T0, H, d))
+    pools, handles = [], []
+    for r in range(n_rep):
+        p = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        h = kivi.kivi_cache_create(cfg, p, pool_bytes)
+        kivi.kivi_append_tokens(h, S, slots, zeros, cu_init, T0, dk, dv, bt, bt.shape[1])
+        pools.append(p)
+        handles.append(h)
+    torch.cuda.synchronize()
+    del dk, dv
+
+    # per-step new tokens and queries
+    total = n_warm + n_steps
+    step_k, step_v, step_q = [], [], []
+    for i in range(total):
+        pos = T0 + i // n_rep
+        step_k.append(dev_u16(np.stack([streams[s][0][pos] for s in range(S)])))
+        step_v.append(dev_u16(np.stack([streams[s][1][pos] for s in range(S)])))
+        step_q.append(dev_u16(w.q_decode(i)))
+    lens = [np.full(S, T0, dtype=np.int64) for _ in range(n_rep)]
+    max_len = T0 + steps_per_rep + 1
+    ws_bytes = kivi.kivi_decode_workspace_bytes(handles[0], S, HQ, max_len)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
+    # per-step length tensors, prepared up front so the timed loop launches only library work
+    lens_before_dev = [torch.from_numpy(np.full(S, T0 + i // n_rep, np.int32)).to(dev) for i in range(total)]
+    lens_after_dev = [torch.from_numpy(np.full(S, T0 + 1 + i // n_rep, np.int32)).to(dev) for i in range(total)]
+    lens_dev0 = torch.from_numpy(np.full(S, T0, np.int32)).to(dev)
+
+    # ---- parity spot check before timing: replica 0 as built, sampled requests ----
+    parity = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.hardware_threads()
+        sample = args.cpu_sample_seqs or max(1, min(S, 8))
+        q0 = w.q_decode(10 ** 6)
+        kivi.kivi_decode_attention(handles[0], S, HQ, dev_u16(q0), slots, lens_dev0, T0, bt, bt.shape[1],
+                                   scale, out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        caches = []
+        for s in range(sample):
+            c = oracle.SeqCache(H, d, w.bits, w.k_group, w.v_group, w.residual, w.dtype, T0 + 1)
+            c.append(streams[s][0][:T0], streams[s][1][:T0])
+            caches.append(c)
+        ref = oracle.attention_all(caches, HQ, q0[:sample], w.dtype, np.arange(sample + 1), scale, False,
+                                   threads=threads)
+        g32 = inputs.bits_to_float(got[:sample], w.dtype).astype(np.float64)
+        r32 = ref.astype(np.float32).astype(np.float64)
+        err = np.abs(g32 - r32)
+        parity = {"requests": sample, "max_abs": float(err.max()),
+                  "max_rel": float((err / np.maximum(np.abs(r32), 1e-3)).max()),
+                  "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
+        # CPU baseline: the oracle's decode step (append one token, attend) on the sample
+        t_cpu = time.perf_counter()
+        for s, c in enumerate(caches):
+            c.append(streams[s][0][T0:T0 + 1], streams[s][1][T0:T0 + 1])
+        oracle.attention_all(caches, HQ, q0[:sample], w.dtype, np.arange(sample + 1), scale, False,
+                             threads=threads)
+        cpu_s = time.perf_counter() - t_cpu
+        cpu_bytes = decode_bytes(np.full(sample, T0 + 1), w)
+        cpu = {"value": cpu_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{sample} of {S} requests (all {HQ} query heads), one decode step "
+                         f"(append 1 token + attention over {T0 + 1} tokens), {cpu_s:.2f} s",
+               "kv_tokens_per_s": sample * (T0 + 1) / cpu_s}
+
+    # ---- timed steps ----
+    stream = torch.cuda.Stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    step_bytes = []
+
+    def one_step(i):
+        r = i % n_rep
+        h = handles[r]
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        kivi.kivi_append_tokens(h, S, slots, lens_before_dev[i], cu_one, 1, step_k[i], step_v[i], bt,
+                                bt.shape[1], stream)
+        e1.record(stream)
+        kivi.kivi_decode_attention(h, S, HQ, step_q[i], slots, lens_after_dev[i], max_len, bt, bt.shape[1],
+                                   scale, out, ws, ws_bytes, stream)
+        e2.record(stream)
+        lens[r] += 1
+        step_bytes.append(decode_bytes(lens[r], w))
+
+    with torch.cuda.stream(stream):
+        for i in range(n_warm):
+            one_step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_warm, total):
+            one_step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
+    append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(n_warm, total)])
+    decode_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(n_warm, total)])
+    timed_bytes = np.array(step_bytes[n_warm:], dtype=np.float64)
+    timed_tokens = S * np.array([T0 + 1 + i // n_rep for i in range(n_warm, total)], dtype=np.float64)
+
+    ms_per_step = wall * 1e3 / n_steps
+    value = float(timed_bytes.sum() / wall / 1e9)
+    dec_avg_s = float(decode_ms.mean()) * 1e-3
+    achieved = float(timed_bytes.mean() / dec_avg_s / 1e9)
+    traffic = measured_traffic(w0.name)
+    res = {
+        "metric": "int4 KIVI decode-attn achieved HBM GB/s (% of peak) and KV tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": n_warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w0.name, "num_seqs": S, "seq_len": T0, "q_heads": HQ, "kv_heads": H,
+                   "head_dim": d, "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
+                   "residual": w.residual, "block_size": w.block_size, "replicas": n_rep,
+                   "step": "append 1 token/request + split-K decode attention + merge"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": float(timed_tokens.sum() / wall),
+        "decode_us_mean": round(float(decode_ms.mean()) * 1e3, 2),
+        "decode_us_p10_p50_p90": [round(float(np.percentile(decode_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "append_us_mean": round(float(append_ms.mean()) * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "kivi_decode_attention (split kernel + merge kernel)",
+                     "bytes_per_launch": int(timed_bytes.mean())},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "input_gen_s": round(gen_s, 1),
+    }
+    for h in handles:
+        kivi.kivi_cache_destroy(h)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * kivi.h - C ABI of a KIVI-style low-bit KV cache with paged attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("4.4 KV Cache 量化", sections 3.1 and 3.2):
+ *   - Key is quantised per channel: for each channel, G consecutive tokens
+ *     share one (scale, zero-point) pair.
+ *   - Value is quantised per token: for each token, Gv consecutive channels
+ *     share one pair.
+ *   - Inside a group the map is min/max asymmetric with b in {2, 4} bits:
+ *       scale = (max - min) / (2^b - 1), zero = min, both stored as fp16,
+ *       code  = clamp(round_half_even((x - zero) / scale), 0, 2^b - 1),
+ *     computed in IEEE single precision against the stored fp16 pair.
+ *   - New tokens first enter a full-precision residual. Key tokens are
+ *     quantised in one batch of R tokens (R/G groups) once R have gathered.
+ *     Value keeps the newest R tokens; each new token pushes the oldest one
+ *     out, and that token is quantised.
+ *   - Attention reads the quantised history and the residual together and
+ *     restores values on read ("给 KV cache 减肥", section 3.1;
+ *     "4.4 KV Cache 量化", section 2: P = softmax(Q K^T / sqrt(d)), out = P V).
+ * After T tokens a sequence holds T_K = R*floor(T/R) quantised Key tokens and
+ * T_V = max(0, T - R) quantised Value tokens; the rest is residual.
+ *
+ * Conventions
+ *   - Pointers named d_* are device memory on the current HIP device. All
+ *     other pointers are host memory.
+ *   - `stream` is a hipStream_t passed as void* (0 = the null stream). Calls
+ *     that launch work are asynchronous on that stream and return once the
+ *     launches are queued.
+ *   - Every argument check happens before any launch; a call that returns an
+ *     error has launched nothing and changed nothing.
+ *   - Ids read from device memory (slot ids, block ids) are range-checked in
+ *     the kernels: a block id outside [0, num_blocks) or a slot id outside
+ *     [0, max_seqs) is skipped (no memory outside the pool is touched), and
+ *     the results for that sequence are unspecified.
+ *   - Only head_dim 128 is supported (the product pages restrict their
+ *     backend to head_dim 128 standard attention and fail fast otherwise);
+ *     anything else is KIVI_ERR_UNSUPPORTED, never silently ignored.
+ *   - Thread safety: calls on different caches may run concurrently. Calls
+ *     on one cache must not overlap on the device in ways that race on the
+ *     same sequence (the caller orders them, e.g. on one stream).
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kivi_status {
+    KIVI_OK = 0,
+    KIVI_ERR_INVALID_ARG = 1,    /* null/misaligned pointer, negative count, bad stride */
+    KIVI_ERR_UNSUPPORTED = 2,    /* configuration outside what the library implements */
+    KIVI_ERR_POOL_TOO_SMALL = 3, /* pool_bytes below kivi_cache_pool_bytes() */
+    KIVI_ERR_WORKSPACE = 4,      /* workspace missing or smaller than required */
+    KIVI_ERR_DEVICE = 5          /* a HIP call or kernel launch failed */
+} kivi_status;
+
+typedef enum kivi_dtype {
+    KIVI_F16 = 0,  /* IEEE binary16 */
+    KIVI_BF16 = 1  /* bfloat16 (values must lie in the fp16 range: the
+                      scale and zero-point are stored as fp16) */
+} kivi_dtype;
+
+/* Cache configuration (one attention layer).
+ *   num_kv_heads  H_KV >= 1
+ *   head_dim      must be 128
+ *   bits          2 or 4
+ *   k_group       G: Key tokens per (channel) group; a multiple of block_size,
+ *                 and 128 must be divisible by G/block_size
+ *   v_group       Gv: Value channels per (token) group: 16, 32, 64 or 128
+ *   residual      R: residual length in tokens; a multiple of G
+ *   block_size    Bk: tokens per physical page; a multiple of 16
+ *   num_blocks    physical pages in the pool (>= 1)
+ *   max_seqs      residual slots (>= 1); a sequence uses the slot the caller
+ *                 assigns it
+ *   kv_dtype      kivi_dtype of the K/V tokens, the residual and q/out      */
+typedef struct kivi_cache_config {
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t bits;
+    int32_t k_group;
+    int32_t v_group;
+    int32_t residual;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t max_seqs;
+    int32_t kv_dtype;
+} kivi_cache_config;
+
+/* Byte offsets of the sub-arrays inside the pool (each 256-byte aligned) and
+ * their strides. The pool layout (all multi-byte fields little-endian):
+ *
+ *   K codes  [num_blocks][H_KV][code_bytes]   code_bytes = Bk*128*b/8
+ *   V codes  [num_blocks][H_KV][code_bytes]
+ *   K meta   [num_blocks][H_KV][k_meta_bytes] k_meta_bytes = 4*128*Bk/G
+ *   V meta   [num_blocks][H_KV][Bk][128/Gv][2] fp16 (scale, zero)
+ *   K ring   [max_seqs][H_KV][R][128]  kv_dtype, token-major
+ *   V ring   [max_seqs][H_KV][128][R]  kv_dtype, channel-major
+ *
+ * A token at position p of a sequence lives in page block_table[p / Bk], row
+ * p % Bk; in the residual it lives in ring row (K) / column (V) p % R.
+ *
+ * K meta: the G/Bk pages of Key group j (tokens jG .. jG+G-1) each hold the
+ * pairs of nch = 128*Bk/G channels: page i of the group holds channels
+ * [i*nch, (i+1)*nch) as fp16 scale[nch] followed by fp16 zero[nch].
+ *
+ * Code chunk of one (page, head): Bk/16 sub-tiles of 16 tokens, each
+ * 16*128*b/8 bytes. With L = m + 16*j (m, j integers, 0 <= m < 16,
+ * 0 <= j < 4), sub-tile lane slot L is the (4*b)-byte run at offset 4*b*L:
+ *   int4 K: slot L = token m; 32-bit word w (w = 0..3) holds channels
+ *           c0 = 32w + 8j .. c0+7: even channels c0+2e in bits 4e..4e+3,
+ *           odd channels c0+2e+1 in bits 16+4e..16+4e+3 (e = 0..3).
+ *   int4 V: slot L = channels {16t + m : t = 0..7}, tokens 4j..4j+3; word w
+ *           covers channels a = 32w + m and c = 32w + 16 + m. Nibble at bit
+ *           4e: e=0 (a,4j) 1 (a,4j+2) 2 (c,4j) 3 (c,4j+2) 4 (a,4j+1)
+ *           5 (a,4j+3) 6 (c,4j+1) 7 (c,4j+3).
+ *   int2 K: slot L = token m; word w (w = 0..1) holds channel groups
+ *           c0 = 64w + 8j (fields 0..3 and 8..11) and c1 = 64w + 32 + 8j
+ *           (fields 4..7 and 12..15), 2-bit field f at bits 2f: field f<8
+ *           holds channel base + 2(f%4), field 8+f holds base + 2(f%4) + 1,
+ *           base = c0 for f%8 < 4 else c1.
+ *   int2 V: slot L = channels {16t + m}, tokens 4j..4j+3; word w (w = 0..1)
+ *           covers channel tiles t = 4w .. 4w+3; field f (f = 0..7) of the
+ *           low half holds (tile 4w + f/2, token 4j + 2(f%2)) and field 8+f
+ *           holds (tile 4w + f/2, token 4j + 2(f%2) + 1).
+ * The layout lets a lane turn a 32-bit word into fp16 pairs with one
+ * AND-OR per pair (the fp16 bias-exponent trick) and feed matrix cores
+ * directly.                                                                  */
+typedef struct kivi_layout {
+    uint64_t k_codes, v_codes, k_meta, v_meta, k_ring, v_ring;
+    uint64_t total_bytes;
+    uint64_t code_bytes;     /* per (page, head) */
+    uint64_t k_meta_bytes;   /* per (page, head) */
+    uint64_t v_meta_bytes;   /* per (page, head) */
+    uint64_t ring_bytes;     /* per (slot, head), K and V alike */
+} kivi_layout;
+
+typedef struct kivi_cache kivi_cache;
+
+/* Pool size for `cfg` in bytes. Host only; validates exactly as create.
+ * Errors: INVALID_ARG (null), UNSUPPORTED (see kivi_cache_config).            */
+kivi_status kivi_cache_pool_bytes(const kivi_cache_config* cfg, size_t* bytes);
+
+/* Bind a cache to the caller's device pool. The caller allocates and owns
+ * d_pool (256-byte aligned, at least kivi_cache_pool_bytes()) and frees it
+ * after kivi_cache_destroy(). The handle holds host metadata only: no device
+ * allocation, no device work, no synchronisation. The pool's initial
+ * contents do not matter; a sequence's state is given by its length.
+ * Errors: INVALID_ARG, UNSUPPORTED, POOL_TOO_SMALL.                          */
+kivi_status kivi_cache_create(const kivi_cache_config* cfg, void* d_pool, size_t pool_bytes,
+                              kivi_cache** out);
+
+/* Release the handle (NULL-safe). Never touches the pool.                    */
+void kivi_cache_destroy(kivi_cache* cache);
+
+/* Offsets and strides of the pool's sub-arrays.                              */
+kivi_status kivi_cache_layout(const kivi_cache* cache, kivi_layout* out);
+
+/* Append new tokens ("4.4 KV Cache 量化", section 3.2; "给 KV cache 减肥",
+ * section 3.1: quantise before writing).
+ *   num_seqs            sequences in this call (0 is a no-op)
+ *   d_slot_ids[S]       residual slot of each sequence (distinct in a call)
+ *   d_seq_lens_before[S] tokens already in each sequence
+ *   d_cu_new[S+1]       sequence s appends rows d_cu_new[s] .. d_cu_new[s+1]-1
+ *   max_new             host upper bound of d_cu_new[s+1] - d_cu_new[s]
+ *   d_k_new, d_v_new    [total_new][H_KV][128] kv_dtype
+ *   d_block_table       [S][bt_stride] int32 page ids; pages must exist for
+ *                       every position < seq_len_before + n_new
+ * The result equals appending the rows one at a time: Value tokens leaving
+ * the R-token window are quantised per token, the new rows enter the
+ * residual, and every time a sequence's Key residual reaches R tokens those
+ * R tokens are quantised per channel as R/G groups. The library keeps no
+ * per-sequence length: lengths are the caller's.
+ * Errors: INVALID_ARG, DEVICE.                                               */
+kivi_status kivi_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_t* d_slot_ids,
+                               const int32_t* d_seq_lens_before, const int32_t* d_cu_new,
+                               int32_t max_new, const void* d_k_new, const void* d_v_new,
+                               const int32_t* d_block_table, int32_t bt_stride, void* stream);
+
+/* Workspace bytes kivi_decode_attention needs for these sizes.              */
+kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_seq_len, size_t* bytes);
+
+/* Decode attention: one query per sequence ("4.4 KV Cache 量化", section 2,
+ * over the quantised history plus the residual, section 3.2).
+ *   d_q[S][H_Q][128]    kv_dtype; query head hq reads KV head hq / (H_Q/H_KV)
+ *   d_seq_lens[S]       tokens in each sequence (after its append); the query
+ *                       attends all of them
+ *   max_seq_len         host upper bound of d_seq_lens
+ *   softmax_scale       multiplies q.k (1/sqrt(128) for standard attention)
+ *   d_out[S][H_Q][128]  kv_dtype; a sequence of length 0 gets zeros
+ *   d_ws, ws_bytes      device workspace of kivi_decode_workspace_bytes()
+ * H_Q must be a multiple of H_KV with H_Q/H_KV <= 16 (else UNSUPPORTED).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
+kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                  const void* d_q, const int32_t* d_slot_ids,
+                                  const int32_t* d_seq_lens, int32_t max_seq_len,
+                                  const int32_t* d_block_table, int32_t bt_stride,
+                                  float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Workspace bytes kivi_prefill_attention needs (0 today; reserved).          */
+kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t max_q_len,
+                                         int32_t max_seq_len, size_t* bytes);
+
+/* Chunked prefill attention ("4.4 KV Cache 量化", section 2) over the cache
+ * as stored, after the chunk's tokens were appended.
+ *   d_q[total_q][H_Q][128] kv_dtype; rows of sequence s are d_cu_q[s] ..
+ *                       d_cu_q[s+1]-1 and row i sits at position
+ *                       seq_len_s - n_q,s + i
+ *   causal              1: row i attends positions 0..its own; 0: all
+ *   d_out[total_q][H_Q][128] kv_dtype
+ * Other arguments as for kivi_decode_attention.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
+kivi_status kivi_prefill_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                   const int32_t* d_slot_ids, const int32_t* d_seq_lens,
+                                   int32_t max_seq_len, const int32_t* d_block_table,
+                                   int32_t bt_stride, float softmax_scale, int32_t causal,
+                                   void* d_out, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Message for the last failure on the calling thread ("" if none).           */
+const char* kivi_last_error(void);
+
+/* Static name of a status code.                                              */
+const char* kivi_status_string(kivi_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

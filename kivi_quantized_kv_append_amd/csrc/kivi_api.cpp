@@ -1,0 +1,337 @@
+// Host side of the C ABI: configuration checks (fail fast on anything the
+// kernels do not implement), pool layout, argument checks, error reporting.
+// No device memory is allocated here and nothing waits on the device.
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "kivi_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kivi_status fail(kivi_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+kivi_status ok() {
+    g_last_error.clear();
+    return KIVI_OK;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255u); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks every field; fills the layout on success.
+kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
+    if (!cfg) return fail(KIVI_ERR_INVALID_ARG, "config is NULL");
+    const kivi_cache_config& c = *cfg;
+    if (c.head_dim != kivi::kHeadDim)
+        return fail(KIVI_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", c.head_dim);
+    if (c.bits != 2 && c.bits != 4)
+        return fail(KIVI_ERR_UNSUPPORTED, "bits %d unsupported (2 or 4)", c.bits);
+    if (c.num_kv_heads < 1 || c.num_kv_heads > 1024)
+        return fail(KIVI_ERR_UNSUPPORTED, "num_kv_heads %d outside [1, 1024]", c.num_kv_heads);
+    if (c.block_size < 16 || c.block_size > 1024 || c.block_size % 16)
+        return fail(KIVI_ERR_UNSUPPORTED, "block_size %d must be a multiple of 16 in [16, 1024]",
+                    c.block_size);
+    if (c.k_group < c.block_size || c.k_group % c.block_size || c.k_group > 256)
+        return fail(KIVI_ERR_UNSUPPORTED,
+                    "k_group %d must be a multiple of block_size %d and at most 256", c.k_group,
+                    c.block_size);
+    {
+        int pages = c.k_group / c.block_size;
+        if (kivi::kHeadDim % pages || (kivi::kHeadDim / pages) % 8)
+            return fail(KIVI_ERR_UNSUPPORTED,
+                        "k_group/block_size = %d must divide 128 into runs of >= 8 channels", pages);
+    }
+    if (c.v_group != 16 && c.v_group != 32 && c.v_group != 64 && c.v_group != 128)
+        return fail(KIVI_ERR_UNSUPPORTED, "v_group %d unsupported (16, 32, 64 or 128)", c.v_group);
+    if (c.residual < c.k_group || c.residual % c.k_group || c.residual > 8192)
+        return fail(KIVI_ERR_UNSUPPORTED,
+                    "residual %d must be a multiple of k_group %d and at most 8192", c.residual,
+                    c.k_group);
+    if (c.num_blocks < 1) return fail(KIVI_ERR_INVALID_ARG, "num_blocks %d < 1", c.num_blocks);
+    if (c.max_seqs < 1) return fail(KIVI_ERR_INVALID_ARG, "max_seqs %d < 1", c.max_seqs);
+    if (c.kv_dtype != KIVI_F16 && c.kv_dtype != KIVI_BF16)
+        return fail(KIVI_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c.kv_dtype);
+
+    const uint64_t H = (uint64_t)c.num_kv_heads;
+    kivi_layout L{};
+    L.code_bytes = (uint64_t)c.block_size * kivi::kHeadDim * c.bits / 8;
+    L.k_meta_bytes = 4ull * kivi::kHeadDim * c.block_size / c.k_group;
+    L.v_meta_bytes = 4ull * c.block_size * (kivi::kHeadDim / c.v_group);
+    L.ring_bytes = 2ull * c.residual * kivi::kHeadDim;
+    uint64_t off = 0;
+    L.k_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
+    L.v_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
+    L.k_meta = off;  off += align256((uint64_t)c.num_blocks * H * L.k_meta_bytes);
+    L.v_meta = off;  off += align256((uint64_t)c.num_blocks * H * L.v_meta_bytes);
+    L.k_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
+    L.v_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
+    L.total_bytes = off;
+    if (lay) *lay = L;
+    return KIVI_OK;
+}
+
+kivi_status check_cache(const kivi_cache* c) {
+    if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+    return KIVI_OK;
+}
+
+kivi_status device_status(int err, const char* what) {
+    if (err != (int)hipSuccess)
+        return fail(KIVI_ERR_DEVICE, "%s: %s", what, hipGetErrorString((hipError_t)err));
+    return ok();
+}
+
+}  // namespace
+
+namespace kivi {
+
+CacheView view_of(const kivi_cache* c) {
+    CacheView v{};
+    const kivi_layout& L = c->layout;
+    v.k_codes = c->pool + L.k_codes;
+    v.v_codes = c->pool + L.v_codes;
+    v.k_meta = c->pool + L.k_meta;
+    v.v_meta = c->pool + L.v_meta;
+    v.k_ring = reinterpret_cast<uint16_t*>(c->pool + L.k_ring);
+    v.v_ring = reinterpret_cast<uint16_t*>(c->pool + L.v_ring);
+    v.H = c->cfg.num_kv_heads;
+    v.bits = c->cfg.bits;
+    v.G = c->cfg.k_group;
+    v.Gv = c->cfg.v_group;
+    v.R = c->cfg.residual;
+    v.Bk = c->cfg.block_size;
+    v.num_blocks = c->cfg.num_blocks;
+    v.max_seqs = c->cfg.max_seqs;
+    v.dtype = c->cfg.kv_dtype;
+    v.code_bytes = (int)L.code_bytes;
+    v.k_meta_bytes = (int)L.k_meta_bytes;
+    v.v_meta_bytes = (int)L.v_meta_bytes;
+    v.ring_elems = (int)(L.ring_bytes / 2);
+    return v;
+}
+
+DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len) {
+    (void)num_q_heads;
+    const int R = c->cfg.residual;
+    const int H = c->cfg.num_kv_heads;
+    const int main_tiles = std::max(0, max_seq_len - R) / kTile;
+    const int pairs = std::max(1, num_seqs * H);
+    // about four waves' worth of work groups per compute unit (256 CUs), at
+    // least 8 tiles (128 tokens) per split
+    int n_splits = (1024 + pairs - 1) / pairs;
+    n_splits = std::min(n_splits, std::max(1, (main_tiles + 7) / 8));
+    n_splits = std::max(1, std::min(n_splits, 256));
+    int tps = std::max(1, (main_tiles + n_splits - 1) / n_splits);
+    n_splits = std::max(1, (main_tiles + tps - 1) / tps);
+    DecodePlan p;
+    p.n_splits = n_splits;
+    p.tiles_per_split = tps;
+    p.ws_bytes = (size_t)num_seqs * num_q_heads * (n_splits + 1) * kPartialStride * sizeof(float);
+    return p;
+}
+
+}  // namespace kivi
+
+extern "C" {
+
+const char* kivi_last_error(void) { return g_last_error.c_str(); }
+
+const char* kivi_status_string(kivi_status s) {
+    switch (s) {
+        case KIVI_OK: return "KIVI_OK";
+        case KIVI_ERR_INVALID_ARG: return "KIVI_ERR_INVALID_ARG";
+        case KIVI_ERR_UNSUPPORTED: return "KIVI_ERR_UNSUPPORTED";
+        case KIVI_ERR_POOL_TOO_SMALL: return "KIVI_ERR_POOL_TOO_SMALL";
+        case KIVI_ERR_WORKSPACE: return "KIVI_ERR_WORKSPACE";
+        case KIVI_ERR_DEVICE: return "KIVI_ERR_DEVICE";
+    }
+    return "KIVI_ERR_UNKNOWN";
+}
+
+kivi_status kivi_cache_pool_bytes(const kivi_cache_config* cfg, size_t* bytes) {
+    if (!bytes) return fail(KIVI_ERR_INVALID_ARG, "bytes is NULL");
+    kivi_layout L;
+    kivi_status s = check_config(cfg, &L);
+    if (s != KIVI_OK) return s;
+    if (L.total_bytes > (uint64_t)std::numeric_limits<size_t>::max())
+        return fail(KIVI_ERR_UNSUPPORTED, "pool size overflows size_t");
+    *bytes = (size_t)L.total_bytes;
+    return ok();
+}
+
+kivi_status kivi_cache_create(const kivi_cache_config* cfg, void* d_pool, size_t pool_bytes,
+                              kivi_cache** out) {
+    if (!out) return fail(KIVI_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    kivi_layout L;
+    kivi_status s = check_config(cfg, &L);
+    if (s != KIVI_OK) return s;
+    if (!d_pool) return fail(KIVI_ERR_INVALID_ARG, "pool is NULL");
+    if (!aligned(d_pool, 256)) return fail(KIVI_ERR_INVALID_ARG, "pool is not 256-byte aligned");
+    if (pool_bytes < L.total_bytes)
+        return fail(KIVI_ERR_POOL_TOO_SMALL, "pool has %zu bytes, needs %llu", pool_bytes,
+                    (unsigned long long)L.total_bytes);
+    kivi_cache* c = new (std::nothrow) kivi_cache;
+    if (!c) return fail(KIVI_ERR_INVALID_ARG, "out of host memory");
+    c->cfg = *cfg;
+    c->layout = L;
+    c->pool = static_cast<uint8_t*>(d_pool);
+    *out = c;
+    return ok();
+}
+
+void kivi_cache_destroy(kivi_cache* cache) { delete cache; }
+
+kivi_status kivi_cache_layout(const kivi_cache* cache, kivi_layout* out) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (!out) return fail(KIVI_ERR_INVALID_ARG, "out is NULL");
+    *out = cache->layout;
+    return ok();
+}
+
+kivi_status kivi_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_t* d_slot_ids,
+                               const int32_t* d_seq_lens_before, const int32_t* d_cu_new,
+                               int32_t max_new, const void* d_k_new, const void* d_v_new,
+                               const int32_t* d_block_table, int32_t bt_stride, void* stream) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_new < 0) return fail(KIVI_ERR_INVALID_ARG, "max_new %d < 0", max_new);
+    if (num_seqs == 0 || max_new == 0) return ok();
+    if (!d_slot_ids || !d_seq_lens_before || !d_cu_new || !d_k_new || !d_v_new || !d_block_table)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_slot_ids, 4) || !aligned(d_seq_lens_before, 4) || !aligned(d_cu_new, 4) ||
+        !aligned(d_block_table, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
+    if (!aligned(d_k_new, 16) || !aligned(d_v_new, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    int err = kivi::launch_append(kivi::view_of(cache), num_seqs, d_slot_ids, d_seq_lens_before,
+                                  d_cu_new, max_new, d_k_new, d_v_new, d_block_table, bt_stride,
+                                  stream);
+    return device_status(err, "append launch");
+}
+
+kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_seq_len, size_t* bytes) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (!bytes) return fail(KIVI_ERR_INVALID_ARG, "bytes is NULL");
+    if (num_seqs < 0 || num_q_heads < 1 || max_seq_len < 0)
+        return fail(KIVI_ERR_INVALID_ARG, "bad sizes (num_seqs %d, num_q_heads %d, max_seq_len %d)",
+                    num_seqs, num_q_heads, max_seq_len);
+    *bytes = kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len).ws_bytes;
+    return ok();
+}
+
+static kivi_status check_heads(const kivi_cache* cache, int32_t num_q_heads) {
+    const int H = cache->cfg.num_kv_heads;
+    if (num_q_heads < 1) return fail(KIVI_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
+    if (num_q_heads % H)
+        return fail(KIVI_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, H);
+    if (num_q_heads / H > kivi::kMaxGqa)
+        return fail(KIVI_ERR_UNSUPPORTED, "%d query heads per KV head (at most %d)",
+                    num_q_heads / H, kivi::kMaxGqa);
+    return KIVI_OK;
+}
+
+kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                  const void* d_q, const int32_t* d_slot_ids,
+                                  const int32_t* d_seq_lens, int32_t max_seq_len,
+                                  const int32_t* d_block_table, int32_t bt_stride,
+                                  float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
+                                  void* stream) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_seq_len < 0) return fail(KIVI_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (!d_q || !d_slot_ids || !d_seq_lens || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_slot_ids, 4) || !aligned(d_seq_lens, 4) || !aligned(d_block_table, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    kivi::DecodePlan plan = kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len);
+    if (!d_ws || ws_bytes < plan.ws_bytes)
+        return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0,
+                    plan.ws_bytes);
+    if (!aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    int err = kivi::launch_decode(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_slot_ids,
+                                  d_seq_lens, d_block_table, bt_stride, softmax_scale, d_out,
+                                  static_cast<float*>(d_ws), plan, stream);
+    return device_status(err, "decode launch");
+}
+
+kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t max_q_len,
+                                         int32_t max_seq_len, size_t* bytes) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (!bytes) return fail(KIVI_ERR_INVALID_ARG, "bytes is NULL");
+    if (num_seqs < 0 || num_q_heads < 1 || max_q_len < 0 || max_seq_len < 0)
+        return fail(KIVI_ERR_INVALID_ARG, "bad sizes");
+    *bytes = 0;
+    return ok();
+}
+
+kivi_status kivi_prefill_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                   const int32_t* d_slot_ids, const int32_t* d_seq_lens,
+                                   int32_t max_seq_len, const int32_t* d_block_table,
+                                   int32_t bt_stride, float softmax_scale, int32_t causal,
+                                   void* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+    (void)d_ws;
+    (void)ws_bytes;
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0)
+        return fail(KIVI_ERR_INVALID_ARG, "bad sizes");
+    if (causal != 0 && causal != 1) return fail(KIVI_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (num_seqs == 0 || max_q_len == 0) return ok();
+    if (!d_q || !d_cu_q || !d_slot_ids || !d_seq_lens || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_cu_q, 4) || !aligned(d_slot_ids, 4) || !aligned(d_seq_lens, 4) ||
+        !aligned(d_block_table, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    int err = kivi::launch_prefill(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_cu_q,
+                                   max_q_len, d_slot_ids, d_seq_lens, max_seq_len, d_block_table,
+                                   bt_stride, softmax_scale, causal, d_out, stream);
+    return device_status(err, "prefill launch");
+}
+
+}  // extern "C"

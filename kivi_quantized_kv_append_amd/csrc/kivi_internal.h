@@ -1,0 +1,63 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kivi.h"
+
+struct kivi_cache {
+    kivi_cache_config cfg;
+    kivi_layout layout;
+    uint8_t* pool;   // caller-owned device memory
+};
+
+namespace kivi {
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 16;          // tokens per matrix-core tile
+constexpr int kMaxGqa = 16;        // query heads per KV head (matrix-core N dimension)
+
+// Launch-time view of a cache: plain values and device pointers.
+struct CacheView {
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    uint8_t* k_meta;
+    uint8_t* v_meta;
+    uint16_t* k_ring;
+    uint16_t* v_ring;
+    int H, bits, G, Gv, R, Bk, num_blocks, max_seqs, dtype;
+    int code_bytes, k_meta_bytes, v_meta_bytes, ring_elems;
+};
+
+CacheView view_of(const kivi_cache* c);
+
+// Split plan for decode: main tiles of a sequence are cut into splits of
+// `tiles_per_split`; one extra split per (sequence, KV head) handles the tail
+// (tiles that touch the residual).
+struct DecodePlan {
+    int n_splits;
+    int tiles_per_split;
+    size_t ws_bytes;
+};
+DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len);
+
+constexpr int kPartialStride = 132;  // floats per partial: m, l, pad, pad, o[128]
+
+// Kernel launchers (return a hipError_t as int).
+int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
+                  const int32_t* seq_lens_before, const int32_t* cu_new, int max_new,
+                  const void* k_new, const void* v_new, const int32_t* block_table, int bt_stride,
+                  void* stream);
+
+int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                  const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
+                  int bt_stride, float softmax_scale, void* out, float* partials,
+                  const DecodePlan& plan, void* stream);
+
+int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                   const int32_t* cu_q, int max_q_len, const int32_t* slot_ids,
+                   const int32_t* seq_lens, int max_seq_len, const int32_t* block_table,
+                   int bt_stride, float softmax_scale, int causal, void* out, void* stream);
+
+}  // namespace kivi

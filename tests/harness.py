@@ -1,0 +1,296 @@
+"""Test-side helpers: drive the C ABI with torch memory, and read a pool back.
+
+``decode_pool`` reads raw pool bytes into logical arrays following the layout
+documented in include/kivi.h (numpy, written independently of the HIP code),
+so GPU caches can be compared bit for bit with the oracle's logical state.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+from kivi_quantized_kv_append_amd import inputs
+from kivi_quantized_kv_append_amd import kivi
+
+D = 128
+
+
+# ---------------------------------------------------------------------------
+# pool layout decoder (numpy)
+# ---------------------------------------------------------------------------
+
+def _u32(b: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(b).view("<u4")
+
+
+def decode_codes(chunks: np.ndarray, bits: int, kind: str) -> np.ndarray:
+    """chunks: [nblk][code_bytes] uint8 of consecutive pages of one (sequence, head).
+    Returns codes [nblk * Bk][128] uint8 in token order."""
+    nblk, cb = chunks.shape
+    nsub = cb // (16 * D * bits // 8)
+    words = _u32(chunks).reshape(nblk, nsub, 4, 16, bits)  # [blk][sub][j][m][w]
+    out = np.zeros((nblk, nsub, 16, D), dtype=np.uint8)
+    jj = np.arange(4)[:, None, None]
+    mm = np.arange(16)[None, :, None]
+    if kind == "k":
+        # slot (j, m) = token m
+        if bits == 4:
+            for w in range(4):
+                c0 = 32 * w + 8 * np.arange(4)  # per j
+                for e in range(4):
+                    lo = (words[..., w] >> (4 * e)) & 0xF
+                    hi = (words[..., w] >> (16 + 4 * e)) & 0xF
+                    for j in range(4):
+                        out[:, :, :, c0[j] + 2 * e] = lo[:, :, j, :]
+                        out[:, :, :, c0[j] + 2 * e + 1] = hi[:, :, j, :]
+        else:
+            for w in range(2):
+                for f in range(8):
+                    lo = (words[..., w] >> (2 * f)) & 0x3
+                    hi = (words[..., w] >> (16 + 2 * f)) & 0x3
+                    for j in range(4):
+                        base = (64 * w + 8 * j) if f < 4 else (64 * w + 32 + 8 * j)
+                        out[:, :, :, base + 2 * (f % 4)] = lo[:, :, j, :]
+                        out[:, :, :, base + 2 * (f % 4) + 1] = hi[:, :, j, :]
+    else:
+        # slot (j, m) = channels 16t + m, tokens 4j .. 4j+3
+        if bits == 4:
+            table = [(0, 0), (0, 2), (1, 0), (1, 2), (0, 1), (0, 3), (1, 1), (1, 3)]  # (a/c, token)
+            for w in range(4):
+                for e, (which, r) in enumerate(table):
+                    val = (words[..., w] >> (4 * e)) & 0xF  # [blk][sub][j][m]
+                    for j in range(4):
+                        ch = 32 * w + 16 * which + np.arange(16)
+                        out[:, :, 4 * j + r, ch] = val[:, :, j, :]
+        else:
+            for w in range(2):
+                for f in range(16):
+                    ff = f & 7
+                    tile = 4 * w + ff // 2
+                    r = 2 * (ff & 1) + (f >> 3)
+                    val = (words[..., w] >> (2 * f)) & 0x3
+                    for j in range(4):
+                        ch = 16 * tile + np.arange(16)
+                        out[:, :, 4 * j + r, ch] = val[:, :, j, :]
+    del jj, mm
+    return out.reshape(nblk * nsub * 16, D)
+
+
+class PoolView:
+    """Logical view of one cache's pool bytes (host copy)."""
+
+    def __init__(self, pool_bytes: np.ndarray, layout: dict, cfg: dict):
+        self.b = pool_bytes
+        self.L = layout
+        self.c = cfg
+
+    def _pages(self, bt_row, npages):
+        return [int(x) for x in bt_row[:npages]]
+
+    def seq_state(self, bt_row, slot: int, T: int, h: int) -> dict:
+        c, L = self.c, self.L
+        H, bits, G, Gv, R, Bk = c["H"], c["bits"], c["G"], c["Gv"], c["R"], c["Bk"]
+        TK = R * (T // R)
+        TV = max(0, T - R)
+        out = {"T": T, "TK": TK, "TV": TV}
+        cb = L["code_bytes"]
+
+        def chunks(base, pages):
+            return np.stack([self.b[base + (p * H + h) * cb: base + (p * H + h + 1) * cb] for p in pages]) \
+                if pages else np.zeros((0, cb), dtype=np.uint8)
+
+        kp = self._pages(bt_row, TK // Bk)
+        vp = self._pages(bt_row, (TV + Bk - 1) // Bk)
+        out["k_code"] = decode_codes(chunks(L["k_codes"], kp), bits, "k")[:TK]
+        out["v_code"] = decode_codes(chunks(L["v_codes"], vp), bits, "v")[:TV]
+        # Key meta: page i of group jg holds channels [i*nch, (i+1)*nch)
+        nch = D * Bk // G
+        ks = np.zeros((TK // G, D), dtype=np.uint16)
+        kz = np.zeros((TK // G, D), dtype=np.uint16)
+        mb = L["k_meta_bytes"]
+        for jg in range(TK // G):
+            for i in range(G // Bk):
+                p = int(bt_row[jg * G // Bk + i])
+                raw = self.b[L["k_meta"] + (p * H + h) * mb: L["k_meta"] + (p * H + h + 1) * mb].view("<u2")
+                ks[jg, i * nch:(i + 1) * nch] = raw[:nch]
+                kz[jg, i * nch:(i + 1) * nch] = raw[nch:2 * nch]
+        out["k_s"], out["k_z"] = ks, kz
+        ng = D // Gv
+        vmb = L["v_meta_bytes"]
+        vs = np.zeros((TV, ng), dtype=np.uint16)
+        vz = np.zeros((TV, ng), dtype=np.uint16)
+        for t in range(0, TV, Bk):
+            p = int(bt_row[t // Bk])
+            raw = self.b[L["v_meta"] + (p * H + h) * vmb: L["v_meta"] + (p * H + h + 1) * vmb]
+            raw = raw.view("<u2").reshape(Bk, ng, 2)
+            n = min(Bk, TV - t)
+            vs[t:t + n] = raw[:n, :, 0]
+            vz[t:t + n] = raw[:n, :, 1]
+        out["v_s"], out["v_z"] = vs, vz
+        # residual rings
+        rb = L["ring_bytes"]
+        kr = self.b[L["k_ring"] + (slot * H + h) * rb: L["k_ring"] + (slot * H + h + 1) * rb].view("<u2").reshape(R, D)
+        vr = self.b[L["v_ring"] + (slot * H + h) * rb: L["v_ring"] + (slot * H + h + 1) * rb].view("<u2").reshape(D, R)
+        out["k_res"] = np.stack([kr[p % R] for p in range(TK, T)]) if T > TK else np.zeros((0, D), np.uint16)
+        out["v_res"] = np.stack([vr[:, p % R] for p in range(TV, T)]) if T > TV else np.zeros((0, D), np.uint16)
+        return out
+
+
+def compare_seq_state(gpu: dict, orc: oracle.SeqCache, h: int, label: str = ""):
+    """Bitwise comparison of one (sequence, head) state with the oracle's."""
+    a = orc.arrays()
+    T, TK, TV = orc.state()
+    assert (gpu["T"], gpu["TK"], gpu["TV"]) == (T, TK, TV), label
+    G = orc.G
+    checks = [
+        ("k_code", gpu["k_code"], a["k_code"][h, :TK]),
+        ("k_s", gpu["k_s"], a["k_s"][h, :TK // G]),
+        ("k_z", gpu["k_z"], a["k_z"][h, :TK // G]),
+        ("v_code", gpu["v_code"], a["v_code"][h, :TV]),
+        ("v_s", gpu["v_s"], a["v_s"][h, :TV]),
+        ("v_z", gpu["v_z"], a["v_z"][h, :TV]),
+        ("k_res", gpu["k_res"], a["k_raw"][h, TK:T]),
+        ("v_res", gpu["v_res"], a["v_raw"][h, TV:T]),
+    ]
+    for name, g, o in checks:
+        assert g.shape == o.shape, f"{label} {name}: shape {g.shape} vs {o.shape}"
+        if not np.array_equal(g, o):
+            bad = np.argwhere(g != o)
+            raise AssertionError(f"{label} {name}: {len(bad)} mismatches, first at {bad[:5].tolist()} "
+                                 f"gpu={g[tuple(bad[0])]} oracle={o[tuple(bad[0])]}")
+
+
+# ---------------------------------------------------------------------------
+# GPU cache driven through the C ABI
+# ---------------------------------------------------------------------------
+
+class GpuCache:
+    def __init__(self, w: inputs.Workload, device="cuda", fill_garbage: bool = True, num_blocks=None):
+        import torch
+        self.torch = torch
+        self.w = w
+        self.device = device
+        self.cfg_dict = {"H": w.num_kv_heads, "bits": w.bits, "G": w.k_group, "Gv": w.v_group,
+                         "R": w.residual, "Bk": w.block_size}
+        nb = num_blocks or w.num_blocks
+        self.cfg = kivi.make_config(w.num_kv_heads, w.bits, w.k_group, w.v_group, w.residual,
+                                    w.block_size, nb, w.num_seqs, w.dtype)
+        self.nbytes = kivi.kivi_cache_pool_bytes(self.cfg)
+        if fill_garbage:
+            g = torch.Generator(device="cpu").manual_seed(123)
+            self.pool = torch.randint(0, 256, (self.nbytes,), dtype=torch.uint8, generator=g).to(device)
+        else:
+            self.pool = torch.zeros(self.nbytes, dtype=torch.uint8, device=device)
+        self.handle = kivi.kivi_cache_create(self.cfg, self.pool, self.nbytes)
+        self.layout = kivi.kivi_cache_layout(self.handle)
+        self.bt_np = w.block_table()
+        self.bt = torch.from_numpy(self.bt_np).to(device)
+        self.slots = torch.arange(w.num_seqs, dtype=torch.int32, device=device)
+        self.lens = np.zeros(w.num_seqs, dtype=np.int64)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            kivi.kivi_cache_destroy(h)
+            self.handle = None
+
+    def t(self, a, dtype=None):
+        torch = self.torch
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a).to(self.device) if dtype is None else \
+            torch.from_numpy(a).to(device=self.device, dtype=dtype)
+
+    def append(self, rows_k: list, rows_v: list, seqs=None, stream=None):
+        """rows_k[i], rows_v[i]: [n_i][H][128] uint16 for sequence seqs[i]."""
+        torch = self.torch
+        seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)
+        ns = [r.shape[0] for r in rows_k]
+        cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+        H = self.w.num_kv_heads
+        k = np.concatenate(rows_k) if cu[-1] else np.zeros((0, H, D), np.uint16)
+        v = np.concatenate(rows_v) if cu[-1] else np.zeros((0, H, D), np.uint16)
+        dk = self.t(k.view(np.int16)) if k.size else torch.zeros(16, dtype=torch.int16, device=self.device)
+        dv = self.t(v.view(np.int16)) if v.size else torch.zeros(16, dtype=torch.int16, device=self.device)
+        sl = self.t(self.lens[seqs].astype(np.int32))
+        slots = self.t(np.asarray(seqs, dtype=np.int32))
+        bt = self.t(self.bt_np[seqs])
+        kivi.kivi_append_tokens(self.handle, len(seqs), slots, sl, self.t(cu), int(max(ns) if ns else 0),
+                                dk, dv, bt, bt.shape[1], stream)
+        for s, n in zip(seqs, ns):
+            self.lens[s] += n
+        return dk, dv
+
+    def decode(self, q_bits: np.ndarray, scale: float, seqs=None, max_seq_len=None):
+        torch = self.torch
+        seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)
+        HQ = self.w.num_q_heads
+        q = self.t(np.ascontiguousarray(q_bits).view(np.int16))
+        out = torch.zeros((len(seqs), HQ, D), dtype=torch.int16, device=self.device)
+        msl = int(self.lens[seqs].max()) if max_seq_len is None else max_seq_len
+        ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, len(seqs), HQ, msl)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        bt = self.t(self.bt_np[seqs])
+        kivi.kivi_decode_attention(self.handle, len(seqs), HQ, q, self.t(np.asarray(seqs, np.int32)),
+                                   self.t(self.lens[seqs].astype(np.int32)), msl, bt, bt.shape[1],
+                                   scale, out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
+    def prefill(self, q_bits: np.ndarray, cu_q: np.ndarray, scale: float, causal=True, seqs=None):
+        torch = self.torch
+        seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)
+        HQ = self.w.num_q_heads
+        q = self.t(np.ascontiguousarray(q_bits).view(np.int16))
+        out = torch.zeros((q_bits.shape[0], HQ, D), dtype=torch.int16, device=self.device)
+        bt = self.t(self.bt_np[seqs])
+        mql = int(np.diff(cu_q).max())
+        msl = int(self.lens[seqs].max())
+        ws_bytes = kivi.kivi_prefill_workspace_bytes(self.handle, len(seqs), HQ, mql, msl)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        kivi.kivi_prefill_attention(self.handle, len(seqs), HQ, q, self.t(cu_q.astype(np.int32)), mql,
+                                    self.t(np.asarray(seqs, np.int32)),
+                                    self.t(self.lens[seqs].astype(np.int32)), msl, bt, bt.shape[1],
+                                    scale, int(causal), out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
+    def pool_view(self) -> PoolView:
+        self.torch.cuda.synchronize()
+        return PoolView(self.pool.cpu().numpy(), self.layout, self.cfg_dict)
+
+
+def oracle_caches(w: inputs.Workload, lens=None):
+    """One oracle SeqCache per request, filled with the first `lens[s]` tokens of its stream."""
+    lens = w.seq_lens if lens is None else lens
+    out = []
+    for s in range(w.num_seqs):
+        c = oracle.SeqCache(w.num_kv_heads, D, w.bits, w.k_group, w.v_group, w.residual, w.dtype,
+                            int(w.final_lens[s]))
+        k, v = w.kv_stream(s, 0, int(lens[s]))
+        c.append(k, v)
+        out.append(c)
+    return out
+
+
+def out_to_f32(bits: np.ndarray, dtype: int) -> np.ndarray:
+    return inputs.bits_to_float(bits, dtype)
+
+
+def check_attention(got_bits: np.ndarray, ref: np.ndarray, dtype: int, atol=2e-3, rtol=1e-2, label=""):
+    """|o - r| <= atol + rtol |r| elementwise (fp32 compare); returns (max_abs, max_rel)."""
+    got = out_to_f32(got_bits, dtype).astype(np.float64)
+    ref = ref.astype(np.float32).astype(np.float64)
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err / np.maximum(np.abs(ref), 1e-3)).max()) if err.size else 0.0
+    if bad.any():
+        idx = np.argwhere(bad)[:5].tolist()
+        raise AssertionError(f"{label}: {int(bad.sum())} of {bad.size} outside tolerance; max_abs {max_abs:.3g} "
+                             f"max_rel {max_rel:.3g}; first {idx}")
+    return max_abs, max_rel
+
+
+SCALE = 1.0 / math.sqrt(D)

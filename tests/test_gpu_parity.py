@@ -1,0 +1,114 @@
+"""GPU parity: append (bit-exact cache state) and decode attention (tolerance)
+against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from kivi_quantized_kv_append_amd import inputs
+from harness import (SCALE, GpuCache, check_attention, compare_seq_state, oracle_caches)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _variant(cfg_id=1, **over):
+    return inputs.config(cfg_id, **over)
+
+
+def _append_and_compare(w, plan, compare_every=True, decode_every=False, seqs_q=None):
+    """Append the streams in chunks (plan[i] = tokens per sequence in call i),
+    comparing the whole GPU state with the oracle after each call."""
+    gc = GpuCache(w)
+    orc = [oracle_caches(w, lens=np.zeros(w.num_seqs, dtype=np.int64))[s] for s in range(w.num_seqs)]
+    streams = [w.kv_stream(s) for s in range(w.num_seqs)]
+    pos = np.zeros(w.num_seqs, dtype=np.int64)
+    for step, n in enumerate(plan):
+        ns = [int(min(n, w.final_lens[s] - pos[s])) for s in range(w.num_seqs)]
+        rk = [streams[s][0][pos[s]:pos[s] + ns[s]] for s in range(w.num_seqs)]
+        rv = [streams[s][1][pos[s]:pos[s] + ns[s]] for s in range(w.num_seqs)]
+        gc.append(rk, rv)
+        for s in range(w.num_seqs):
+            orc[s].append(rk[s], rv[s])
+            pos[s] += ns[s]
+        if compare_every or step == len(plan) - 1:
+            pv = gc.pool_view()
+            for s in range(w.num_seqs):
+                for h in range(w.num_kv_heads):
+                    st = pv.seq_state(gc.bt_np[s], s, int(pos[s]), h)
+                    compare_seq_state(st, orc[s], h, label=f"{w.name} step {step} seq {s} head {h}")
+        if decode_every:
+            q = w.q_decode(step)
+            got = gc.decode(q, SCALE)
+            ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1),
+                                       SCALE, False, threads=8)
+            check_attention(got, ref, w.dtype, label=f"{w.name} decode step {step}")
+    return gc, orc
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_config1_append_stream_bitexact_and_decode(bits):
+    w = _variant(1, bits=bits)
+    plan = [1] * 40 + [7, 33, 64, 1, 1, 110]
+    _append_and_compare(w, plan, decode_every=True)
+
+
+@pytest.mark.parametrize("bits,G,Gv,R,Bk,H,dtype", [
+    (4, 16, 16, 48, 16, 2, inputs.F16),
+    (2, 64, 64, 128, 32, 3, inputs.F16),
+    (4, 128, 128, 128, 16, 2, inputs.BF16),
+    (2, 32, 128, 64, 16, 1, inputs.BF16),
+])
+def test_append_variants_bitexact(bits, G, Gv, R, Bk, H, dtype):
+    w = _variant(1, bits=bits, k_group=G, v_group=Gv, residual=R, block_size=Bk, num_kv_heads=H,
+                 num_q_heads=4 * H, dtype=dtype, num_seqs=3, seq_lens=[700, 333, 517], shuffle=True,
+                 pool_factor=1.5, n_outlier=2)
+    plan = [1, 1, 5, 16, 63, 1, 1, 128, 200, 3, 300]
+    _append_and_compare(w, plan, decode_every=True)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_ragged_batch_llama_shape(bits):
+    """Reduced Llama-3-8B shape (32 Q / 8 KV heads): ragged lengths around the
+    residual and tile edges, one bulk append then decode."""
+    lens = [0, 1, 15, 16, 127, 128, 129, 143, 144, 1000, 2049]
+    w = _variant(2, bits=bits, num_seqs=len(lens), seq_lens=lens, shuffle=True, pool_factor=1.25)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(w.num_seqs)])
+    gc.append(list(rk), list(rv))
+    pv = gc.pool_view()
+    for s in range(w.num_seqs):
+        for h in (0, 7):
+            compare_seq_state(pv.seq_state(gc.bt_np[s], s, int(w.seq_lens[s]), h), orc[s], h,
+                              label=f"seq {s} head {h}")
+    q = w.q_decode(0)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False,
+                               threads=8)
+    check_attention(got, ref, w.dtype, label="ragged decode")
+    # a zero-length sequence gets zeros
+    assert np.all(got[0] == 0)
+
+
+@pytest.mark.parametrize("gqa", [1, 7, 16])
+def test_decode_gqa_ratios(gqa):
+    w = _variant(3, num_seqs=2, seq_lens=[1500, 777], num_kv_heads=2, num_q_heads=2 * gqa)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(w.num_seqs)])
+    gc.append(list(rk), list(rv))
+    q = w.q_decode(1)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, [0, 1, 2], SCALE, False, threads=8)
+    check_attention(got, ref, w.dtype, label=f"gqa {gqa}")
+
+
+def test_decode_bf16_qwen_shape():
+    w = _variant(5, num_seqs=2, seq_lens=[1300, 2000], extra_tokens=0)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(w.num_seqs)])
+    gc.append(list(rk), list(rv))
+    q = w.q_decode(0)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, [0, 1, 2], SCALE, False, threads=8)
+    check_attention(got, ref, w.dtype, label="bf16 decode")
