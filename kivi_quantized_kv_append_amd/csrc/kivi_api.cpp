@@ -49,6 +49,9 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     if (c.block_size < 16 || c.block_size > 1024 || c.block_size % 16)
         return fail(KIVI_ERR_UNSUPPORTED, "block_size %d must be a multiple of 16 in [16, 1024]",
                     c.block_size);
+    if ((c.block_size & (c.block_size - 1)) || (c.k_group & (c.k_group - 1)))
+        return fail(KIVI_ERR_UNSUPPORTED, "block_size %d and k_group %d must be powers of two", c.block_size,
+                    c.k_group);
     if (c.k_group < c.block_size || c.k_group % c.block_size || c.k_group > 256)
         return fail(KIVI_ERR_UNSUPPORTED,
                     "k_group %d must be a multiple of block_size %d and at most 256", c.k_group,
@@ -84,6 +87,10 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     L.k_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
     L.v_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
     L.total_bytes = off;
+    // decode addresses code pages with 32-bit offsets
+    if ((uint64_t)c.num_blocks * H * L.code_bytes >= (1ull << 32))
+        return fail(KIVI_ERR_UNSUPPORTED, "code sub-array of %llu bytes exceeds 4 GiB",
+                    (unsigned long long)((uint64_t)c.num_blocks * H * L.code_bytes));
     if (lay) *lay = L;
     return KIVI_OK;
 }
@@ -129,22 +136,29 @@ CacheView view_of(const kivi_cache* c) {
 }
 
 DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len) {
-    (void)num_q_heads;
     const int R = c->cfg.residual;
     const int H = c->cfg.num_kv_heads;
+    const int tpg = c->cfg.k_group / kTile;
+    const int gqa = std::max(1, std::min(kMaxGqa, num_q_heads / H));
     const int main_tiles = std::max(0, max_seq_len - R) / kTile;
     const int pairs = std::max(1, num_seqs * H);
-    // about four waves' worth of work groups per compute unit (256 CUs), at
-    // least 8 tiles (128 tokens) per split
-    int n_splits = (1024 + pairs - 1) / pairs;
+    const int lds_groups = decode_lds_groups(gqa);
+    // one round of resident work groups (256 CUs x 3, or x 2 for narrow
+    // Value groups), at least 8 tiles (128 tokens) per split
+    const int resident = (c->cfg.v_group == kHeadDim ? 3 : 2) * 256;
+    int n_splits = std::max(1, (resident + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (main_tiles + 7) / 8));
     n_splits = std::max(1, std::min(n_splits, 256));
     int tps = std::max(1, (main_tiles + n_splits - 1) / n_splits);
     n_splits = std::max(1, (main_tiles + tps - 1) / tps);
+    (void)tpg;
     DecodePlan p;
     p.n_splits = n_splits;
     p.tiles_per_split = tps;
-    p.ws_bytes = (size_t)num_seqs * num_q_heads * (n_splits + 1) * kPartialStride * sizeof(float);
+    p.lds_groups = lds_groups;
+    p.lds_bytes = decode_lds_bytes(gqa, lds_groups);
+    p.counter_floats = (((size_t)num_seqs * H + 63) / 64) * 64;  // 256-byte aligned
+    p.ws_bytes = (p.counter_floats + (size_t)num_seqs * num_q_heads * n_splits * kPartialStride) * sizeof(float);
     return p;
 }
 

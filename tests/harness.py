@@ -230,7 +230,7 @@ class GpuCache:
         out = torch.zeros((len(seqs), HQ, D), dtype=torch.int16, device=self.device)
         msl = int(self.lens[seqs].max()) if max_seq_len is None else max_seq_len
         ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, len(seqs), HQ, msl)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
         bt = self.t(self.bt_np[seqs])
         kivi.kivi_decode_attention(self.handle, len(seqs), HQ, q, self.t(np.asarray(seqs, np.int32)),
                                    self.t(self.lens[seqs].astype(np.int32)), msl, bt, bt.shape[1],
