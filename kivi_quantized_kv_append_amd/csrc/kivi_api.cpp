@@ -138,25 +138,18 @@ CacheView view_of(const kivi_cache* c) {
 DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len) {
     const int R = c->cfg.residual;
     const int H = c->cfg.num_kv_heads;
-    const int tpg = c->cfg.k_group / kTile;
     const int gqa = std::max(1, std::min(kMaxGqa, num_q_heads / H));
     const int main_tiles = std::max(0, max_seq_len - R) / kTile;
     const int pairs = std::max(1, num_seqs * H);
-    const int lds_groups = decode_lds_groups(gqa);
-    // one round of resident work groups (256 CUs x 3, or x 2 for narrow
-    // Value groups), at least 8 tiles (128 tokens) per split
-    const int resident = (c->cfg.v_group == kHeadDim ? 3 : 2) * 256;
+    // one round of resident work groups (256 CUs x 2), at least
+    // kMinSplitTiles main tiles per split
+    const int resident = 2 * 256;
     int n_splits = std::max(1, (resident + pairs / 2) / pairs);
-    n_splits = std::min(n_splits, std::max(1, (main_tiles + 7) / 8));
+    n_splits = std::min(n_splits, std::max(1, (main_tiles + kMinSplitTiles - 1) / kMinSplitTiles));
     n_splits = std::max(1, std::min(n_splits, 256));
-    int tps = std::max(1, (main_tiles + n_splits - 1) / n_splits);
-    n_splits = std::max(1, (main_tiles + tps - 1) / tps);
-    (void)tpg;
     DecodePlan p;
     p.n_splits = n_splits;
-    p.tiles_per_split = tps;
-    p.lds_groups = lds_groups;
-    p.lds_bytes = decode_lds_bytes(gqa, lds_groups);
+    p.lds_bytes = decode_lds_bytes(gqa);
     p.counter_floats = (((size_t)num_seqs * H + 63) / 64) * 64;  // 256-byte aligned
     p.ws_bytes = (p.counter_floats + (size_t)num_seqs * num_q_heads * n_splits * kPartialStride) * sizeof(float);
     return p;

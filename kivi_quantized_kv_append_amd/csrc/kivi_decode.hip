@@ -43,7 +43,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kHalf = 2;  // tiles per load buffer; two buffers per wave
+// Tiles per load buffer (two buffers per wave): deeper for the lighter
+// Value metadata of wide Value groups.
+template <int NG>
+__host__ __device__ constexpr int buffer_tiles() { return NG == 1 ? 4 : (NG <= 4 ? 2 : 1); }
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -59,11 +62,9 @@ struct DecodeArgs {
     float* partials;
     int* counters;    // one per (sequence, KV head); zero between calls
     int n_splits;
-    int tiles_per_split;
-    int lds_groups;   // Key groups whose query tables fit the work group's LDS
     int tpg_shift;    // log2(tiles per Key group)
     int tpp_shift;    // log2(tiles per page)
-    uint32_t code_array_bytes, vmeta_array_bytes;
+    uint32_t code_array_bytes, vmeta_array_bytes, kmeta_array_bytes;
     uint16_t* out;
 };
 
@@ -94,8 +95,12 @@ __device__ __forceinline__ h4 make_h4(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(h4, (u2){a, b});
 }
 
-// x = hi + lo with both parts fp16 (about 22 significant bits together)
+// x = hi + lo with both parts fp16 (about 22 significant bits together).
+// x is pinned to a register first: the compiler may otherwise fold the
+// product that makes x into a single-rounding conversion for one use of hi
+// and not for another, and then hi + lo misses x by an fp16 ulp of hi.
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+    asm volatile("" : "+v"(x));
     hi = (_Float16)x;
     lo = (_Float16)(x - (float)hi);
 }
@@ -212,43 +217,23 @@ __device__ __forceinline__ float v_inv_factor(int t, int r) {
     else return 1.0f / (float)(1 << (2 * (2 * (t & 1) + (r >> 1))));
 }
 
-// LDS layout of one work group (dynamic shared memory), in fp16 rows of
+// Per-wave LDS (dynamic shared memory, one region per wave), fp16 rows of
 // kQRow elements (272 bytes: the 16-byte pad spreads rows over banks):
-//   zero row | q[g] | per group: table[g][hi, lo] rows, Z[128], bias[16] f32
-// The merge buffers of the epilogue reuse the same memory.
+//   q rows [g] | Key-group table rows [g][hi, lo] | bias [16] f32
+// The epilogue reuses the whole work group's memory for the wave merge.
 constexpr int kQRow = 136;
 constexpr int kRowBytes = kQRow * 2;
 
-__host__ __device__ constexpr int group_lds_bytes(int g) { return g * 2 * kRowBytes + 256 + 64; }
-__host__ __device__ constexpr int head_lds_bytes(int g) { return kRowBytes * (g + 1); }
-constexpr int kMergeBytes = kWaves * 16 * 4 * 2 + kWaves * 16 * kHeadDim * 4;
+__host__ __device__ constexpr int wave_lds_bytes(int g) { return 3 * g * kRowBytes + 64; }
+__host__ __device__ constexpr int merge_lds_bytes(int g) { return kWaves * g * (kHeadDim + 2) * 4; }
 
-template <int BITS, int NG>
-struct TileRegs {
-    uint32_t k[BITS];
-    uint32_t v[BITS];
-    uint32_t vm[4 * NG];
-};
-
-template <int BITS, int NG>
-__device__ __forceinline__ void load_tile(TileRegs<BITS, NG>& r, const uint8_t* kslot, const uint8_t* vslot,
-                                          const uint32_t* vmeta) {
-    if constexpr (BITS == 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kslot);
-        const uint4 b = *reinterpret_cast<const uint4*>(vslot);
-        r.k[0] = a.x; r.k[1] = a.y; r.k[2] = a.z; r.k[3] = a.w;
-        r.v[0] = b.x; r.v[1] = b.y; r.v[2] = b.z; r.v[3] = b.w;
-    } else {
-        const uint2 a = *reinterpret_cast<const uint2*>(kslot);
-        const uint2 b = *reinterpret_cast<const uint2*>(vslot);
-        r.k[0] = a.x; r.k[1] = a.y;
-        r.v[0] = b.x; r.v[1] = b.y;
-    }
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-        const uint4 m = reinterpret_cast<const uint4*>(vmeta)[q];
-        r.vm[4 * q + 0] = m.x; r.vm[4 * q + 1] = m.y; r.vm[4 * q + 2] = m.z; r.vm[4 * q + 3] = m.w;
-    }
+// Sum over the 16 lanes of a row (lanes 16r .. 16r+15), every lane gets it.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+    return x;
 }
 
 // Shared state of one work group: the sequence, the KV head, its lengths.
@@ -276,44 +261,33 @@ __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
     return c;
 }
 
+// Physical page of tile t, or -1 when the table has none (tile skipped).
 __device__ __forceinline__ int page_of_tile(const DecodeArgs& a, const WgCtx& c, int t) {
-    const int bi = t / (a.v.Bk / kTile);
-    if (bi >= c.bt_len) return -1;
+    const int bi = t >> a.tpp_shift;
+    if (t < 0 || bi >= c.bt_len) return -1;
     const int blk = c.bt[bi];
     return (blk >= 0 && blk < a.v.num_blocks) ? blk : -1;
 }
 
-// q of the g query heads as fp16 rows after a zero row (padding heads read the
-// zero row); bf16 queries convert exactly within the fp16 range.
-// q of the g query heads as fp16 rows after a zero row (bf16 queries convert
-// exactly within the fp16 range). Loaded to registers first, stored later,
-// so the load overlaps other round trips. Rows hold 16 chunks of 8 channels.
-constexpr int kQueryRounds = 2;  // (16 + 1) rows x 16 chunks <= 2 x 256 threads
-struct QueryLoads {
-    uint4 v[kQueryRounds];
-};
-
+// The g query rows of this KV head, converted to fp16 (bf16 queries are
+// exact in fp16 inside its range), into the wave's q rows.
 template <int DT>
-__device__ __forceinline__ void query_load(const DecodeArgs& a, const WgCtx& c, QueryLoads& ql) {
+__device__ __forceinline__ void load_query(const DecodeArgs& a, const WgCtx& c, uint16_t* lq) {
+    const int lane = threadIdx.x & 63;
+    uint4 v[4];
 #pragma unroll
-    for (int r = 0; r < kQueryRounds; ++r) {
-        const int idx = threadIdx.x + r * kThreads;
-        const int hn = idx / 16 - 1, k = idx % 16;
-        ql.v[r] = (uint4){0, 0, 0, 0};
-        if (hn >= 0 && hn < c.g)
-            ql.v[r] = *reinterpret_cast<const uint4*>(a.q + ((size_t)c.s * a.num_q_heads + c.h * c.g + hn) * kHeadDim +
-                                                      8 * k);
+    for (int r = 0; r < 4; ++r) {  // 16 chunks of 8 channels per row, up to 16 rows
+        const int idx = lane + 64 * r, hn = idx >> 4, k = idx & 15;
+        v[r] = (uint4){0, 0, 0, 0};
+        if (hn < c.g)
+            v[r] = *reinterpret_cast<const uint4*>(a.q + ((size_t)c.s * a.num_q_heads + c.h * c.g + hn) * kHeadDim +
+                                                   8 * k);
     }
-}
-
-template <int DT>
-__device__ __forceinline__ void query_store(const WgCtx& c, const QueryLoads& ql, uint16_t* lds_zero) {
 #pragma unroll
-    for (int r = 0; r < kQueryRounds; ++r) {
-        const int idx = threadIdx.x + r * kThreads;
-        if (idx >= (c.g + 1) * 16) continue;
-        const int row = idx / 16, k = idx % 16;
-        uint4 out = ql.v[r];
+    for (int r = 0; r < 4; ++r) {
+        const int idx = lane + 64 * r, hn = idx >> 4, k = idx & 15;
+        if (hn >= c.g) continue;
+        uint4 out = v[r];
         if constexpr (DT == kBF16) {
             const uint32_t w[4] = {out.x, out.y, out.z, out.w};
             uint32_t o[4];
@@ -325,114 +299,71 @@ __device__ __forceinline__ void query_store(const WgCtx& c, const QueryLoads& ql
             }
             out = {o[0], o[1], o[2], o[3]};
         }
-        *reinterpret_cast<uint4*>(lds_zero + row * kQRow + 8 * k) = out;
+        *reinterpret_cast<uint4*>(lq + hn * kQRow + 8 * k) = out;
     }
 }
 
-constexpr int kTableRounds = 4;  // 8-channel chunks per thread: up to 64 groups per table
-
-// Key-group tables are built in three phases so that their two memory round
-// trips (page ids, then the scale/zero runs) overlap with other loads:
-//   table_pages -> (other loads) -> table_meta -> (other loads) -> table_fill.
-struct TableLoads {
-    int blk[kTableRounds];
-    uint4 sv[kTableRounds], zv[kTableRounds];
-};
-
-template <class GroupOf>
-__device__ __forceinline__ void table_pages(const DecodeArgs& a, const WgCtx& c, int n_groups, GroupOf group_of,
-                                            TableLoads& tl) {
-    const CacheView& V = a.v;
-    const int tpg = V.G / kTile, tpp = V.Bk / kTile;
-    const int nch = kHeadDim * V.Bk / V.G;
-#pragma unroll
-    for (int r = 0; r < kTableRounds; ++r) {
-        const int q = threadIdx.x + r * kThreads;  // 8-channel chunk q % 16 of table slot q / 16
-        const int ch = 8 * (q % 16);
-        const int gi = q < n_groups * 16 ? group_of(q / 16) : -1;
-        tl.blk[r] = gi >= 0 ? page_of_tile(a, c, gi * tpg + (ch / nch) * tpp) : -1;
-    }
+// Byte offset into the Key meta array of this lane's 8-channel run (channels
+// 8 (lane & 15) .. +7) of a Key group, given the physical page holding them.
+__device__ __forceinline__ uint32_t k_meta_off(const CacheView& V, int h, int page, int nch) {
+    const int ch = 8 * (threadIdx.x & 15);
+    return ((uint32_t)max(page, 0) * (uint32_t)V.H + (uint32_t)h) * (uint32_t)V.k_meta_bytes + 2u * (uint32_t)(ch % nch);
 }
 
-__device__ __forceinline__ void table_meta(const DecodeArgs& a, const WgCtx& c, TableLoads& tl) {
-    const CacheView& V = a.v;
-    const int nch = kHeadDim * V.Bk / V.G;
-#pragma unroll
-    for (int r = 0; r < kTableRounds; ++r) {
-        const int ch = 8 * ((threadIdx.x + r * kThreads) % 16);
-        const size_t base = (size_t)(tl.blk[r] >= 0 ? tl.blk[r] : 0) * V.H + c.h;
-        const uint16_t* meta = reinterpret_cast<const uint16_t*>(V.k_meta + base * V.k_meta_bytes);
-        tl.sv[r] = *reinterpret_cast<const uint4*>(meta + (ch % nch));
-        tl.zv[r] = *reinterpret_cast<const uint4*>(meta + nch + (ch % nch));
-    }
-}
-
-// Writes the tables of groups g_first .. g_first+n_groups-1 into slots
-// 0 .. n_groups-1; lds_q must be visible to every thread (barrier before).
-// Ends with a barrier; call it with every thread of the work group.
+// Query table of one Key group, built by one wave into its own LDS rows:
+//   hi/lo rows: Q'[n][c] = q[n][c] s[c] f(c) as an fp16 pair (hi + lo), where
+//   f(c) is the inverse place value of channel c's field in the code words;
+//   bias[n] = sum_c q[n][c] z[c] (fp16 products, fp32 sums).
+// Lane (k = lane & 15, r = lane >> 4) covers channels 8k..8k+7 of heads
+// r, r+4, r+8, r+12. sv/zv: the lane's 8 scales and zero-points. Returns
+// bias[nr] * scale_log2 for this lane's score row nr.
 template <int BITS>
-__device__ __forceinline__ void table_fill(const WgCtx& c, int n_groups, const TableLoads& tl, const uint16_t* lds_q,
-                                           uint8_t* lds_groups) {
-    const int g = c.g, tid = threadIdx.x;
-    const int gbytes = group_lds_bytes(g);
+__device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const uint16_t* lq, uint8_t* lt, float* lbias,
+                                             int nr, float sl2) {
+    const int lane = threadIdx.x & 63, k = lane & 15, r = lane >> 4;
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+    h2 sf[4];
 #pragma unroll
-    for (int r = 0; r < kTableRounds; ++r) {
-        const int q = tid + r * kThreads;
-        if (q >= n_groups * 16) continue;
-        const int gl = q / 16, ch = 8 * (q % 16);
-        const bool ok = tl.blk[r] >= 0;
-        const uint4 sv = ok ? tl.sv[r] : (uint4){0, 0, 0, 0};
-        const uint4 zv = ok ? tl.zv[r] : (uint4){0, 0, 0, 0};
-        uint8_t* gb = lds_groups + gl * gbytes;
-        *reinterpret_cast<uint4*>(gb + g * 2 * kRowBytes + 2 * ch) = zv;
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-        h2 sf[4];
+    for (int e = 0; e < 4; ++e) {
+        const float f = (BITS == 4) ? ((e & 1) ? 0.0625f : 1.0f) : 1.0f / (float)(1 << (2 * e));
+        sf[e] = __builtin_bit_cast(h2, sw[e]) * (h2){(_Float16)f, (_Float16)f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (4 * u >= g) break;  // uniform
+        const int hn = r + 4 * u;
+        const bool ok = hn < g;
+        const uint4 qu = *reinterpret_cast<const uint4*>(lq + (ok ? hn : 0) * kQRow + 8 * k);
+        const uint32_t qw[4] = {qu.x, qu.y, qu.z, qu.w};
+        uint32_t hw[4], lw[4];
+        float zq = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // pair factor of channel pair e of this 8-channel run
-            const float f = (BITS == 4) ? ((e & 1) ? 0.0625f : 1.0f) : 1.0f / (float)(1 << (2 * e));
-            sf[e] = __builtin_bit_cast(h2, sw[e]) * (h2){(_Float16)f, (_Float16)f};
+            const h2 qv = __builtin_bit_cast(h2, qw[e]);
+            const h2 hi = qv * sf[e];
+            const h2 lo = __builtin_elementwise_fma(qv, sf[e], -hi);  // fp16(q s f - hi)
+            hw[e] = __builtin_bit_cast(uint32_t, hi);
+            lw[e] = __builtin_bit_cast(uint32_t, lo);
+            zq = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2, zw[e]), zq, false);
         }
-        for (int hn = 0; hn < g; ++hn) {
-            const uint4 qu = *reinterpret_cast<const uint4*>(lds_q + hn * kQRow + ch);
-            const uint32_t qw[4] = {qu.x, qu.y, qu.z, qu.w};
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const h2 qv = __builtin_bit_cast(h2, qw[e]);
-                // hi = fp16(q s f); lo = fp16(q s f - hi), the fused residual
-                const h2 hi = qv * sf[e];
-                const h2 lo = __builtin_elementwise_fma(qv, sf[e], -hi);
-                hw[e] = __builtin_bit_cast(uint32_t, hi);
-                lw[e] = __builtin_bit_cast(uint32_t, lo);
-            }
-            *reinterpret_cast<uint4*>(gb + (hn * 2 + 0) * kRowBytes + 2 * ch) = (uint4){hw[0], hw[1], hw[2], hw[3]};
-            *reinterpret_cast<uint4*>(gb + (hn * 2 + 1) * kRowBytes + 2 * ch) = (uint4){lw[0], lw[1], lw[2], lw[3]};
+        zq = row_sum16(ok ? zq : 0.0f);
+        if (ok) {
+            *reinterpret_cast<uint4*>(lt + (2 * hn + 0) * kRowBytes + 16 * k) = (uint4){hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<uint4*>(lt + (2 * hn + 1) * kRowBytes + 16 * k) = (uint4){lw[0], lw[1], lw[2], lw[3]};
+            if (k == 0) lbias[hn] = zq;
         }
     }
-    __syncthreads();
-    for (int idx = tid; idx < n_groups * g; idx += kThreads) {
-        const int gl = idx / g, hn = idx % g;
-        const uint8_t* gb = lds_groups + gl * gbytes;
-        float zq = 0.0f;  // sum_c q_c zero_c (exact products, fp32 sum)
-#pragma unroll 4
-        for (int k = 0; k < 16; ++k) {
-            const uint4 zu = *reinterpret_cast<const uint4*>(gb + g * 2 * kRowBytes + 16 * k);
-            const uint4 qu = *reinterpret_cast<const uint4*>(lds_q + hn * kQRow + 8 * k);
-            zq = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, qu.x), __builtin_bit_cast(h2, zu.x), zq, false);
-            zq = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, qu.y), __builtin_bit_cast(h2, zu.y), zq, false);
-            zq = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, qu.z), __builtin_bit_cast(h2, zu.z), zq, false);
-            zq = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, qu.w), __builtin_bit_cast(h2, zu.w), zq, false);
-        }
-        *reinterpret_cast<float*>(lds_groups + gl * gbytes + g * 2 * kRowBytes + 256 + 4 * hn) = zq;
-    }
-    __syncthreads();
+    // LDS operations of one wave complete in order; the fence keeps the
+    // compiler from moving the reads below above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    return lbias[nr] * sl2;
 }
 
 // Per-lane online-softmax state of query head (lane & 15) and its output
 // accumulators O^T[16 t + 4 (lane >> 4) + r][head] held in O[t][r].
 // wsum[gg][vb] sums the value-side weights (hi + lo) of channel group gg and
-// pair-factor variant vb: the codes carry a 1024 offset, so every output
+// pair-factor variant vb: int4 codes carry a 1024 offset, so every output
 // channel holds 1024 * wsum too much until the merge takes it out.
 template <int NG, int NB>
 struct Acc {
@@ -451,11 +382,13 @@ struct Acc {
         for (int t = 0; t < 8; ++t) O[t] = (f4){0.f, 0.f, 0.f, 0.f};
     }
     // Scores of tokens 4j..4j+3 of one tile (exp2 domain) -> weights p.
+    // The rescale branch is taken by the whole wave when any head needs it
+    // (heads that do not get a factor of 1), so it never runs divergent.
     __device__ __forceinline__ void update(const float sc[4], float p[4]) {
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = xor_max(mx);
-        if (mx > m_run) {
-            const float f = __builtin_amdgcn_exp2f(m_run - mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
+            const float f = mx > m_run ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
             l_acc *= f;
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
@@ -465,7 +398,7 @@ struct Acc {
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) O[t] *= f;
-            m_run = mx;
+            m_run = fmaxf(m_run, mx);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
@@ -473,106 +406,97 @@ struct Acc {
     }
 };
 
-// Scale-folded query B-operands of one Key group for this lane (head n,
-// k-slice j), read from the LDS table.
-struct GroupOps {
-    h8 Bh[4], Bl[4];
-    float biasl2;
-    int cur;
-    __device__ __forceinline__ void load(const uint8_t* lds_groups, const uint16_t* lds_zero, int gbytes, int g,
-                                         int gl, int gi, int n, int j, float sl2) {
-        const uint8_t* gb = lds_groups + gl * gbytes;
-        const bool ok = n < g;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int off = 2 * (32 * i + 8 * j);
-            const uint8_t* rh = ok ? gb + (n * 2 + 0) * kRowBytes + off : reinterpret_cast<const uint8_t*>(lds_zero);
-            const uint8_t* rl = ok ? gb + (n * 2 + 1) * kRowBytes + off : reinterpret_cast<const uint8_t*>(lds_zero);
-            Bh[i] = *reinterpret_cast<const h8*>(rh);
-            Bl[i] = *reinterpret_cast<const h8*>(rl);
-        }
-        biasl2 = ok ? reinterpret_cast<const float*>(gb + g * 2 * kRowBytes + 256)[n] * sl2 : 0.0f;
-        cur = gi;
-    }
-};
-
-// Scores (exp2 domain) of a 16-token tile whose Keys are quantised.
+// Scores (exp2 domain) of a 16-token tile whose Keys are quantised: the
+// group's B-operands come straight from the wave's LDS table; two
+// accumulation chains (hi, lo). `row`: the lane's byte offset into the table
+// (head row nr, k-slice 16 j).
 template <int BITS>
-__device__ __forceinline__ void code_scores(const uint32_t* kw, const GroupOps& go, float sl2, float sc[4]) {
-    h8 A[4];
-    unpack_k<BITS>(kw, A);
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], go.Bh[i], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], go.Bl[i], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = acc[r] * sl2 + go.biasl2;
-}
-
-// Same, reading the group's B-operands straight from the LDS table (no
-// register copy of the table); two accumulation chains (hi, lo). `row` is
-// the lane's byte offset into a group table: head row of (n, or n mod g for
-// padding lanes, whose results are never used) plus the k-slice 16 j.
-template <int BITS>
-__device__ __forceinline__ void code_scores_lds(const uint32_t* kw, const uint8_t* gb, int row, int bias_off,
-                                                float sl2, float sc[4]) {
+__device__ __forceinline__ void code_scores(const uint32_t* kw, const uint8_t* lt, int row, float bias_l2, float sl2,
+                                            float sc[4]) {
     h8 A[4];
     unpack_k<BITS>(kw, A);
     f4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const h8 bh = *reinterpret_cast<const h8*>(gb + row + 64 * i);
-        const h8 bl = *reinterpret_cast<const h8*>(gb + row + kRowBytes + 64 * i);
+        const h8 bh = *reinterpret_cast<const h8*>(lt + row + 64 * i);
+        const h8 bl = *reinterpret_cast<const h8*>(lt + row + kRowBytes + 64 * i);
         ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bh, ah, 0, 0, 0);
         al = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bl, al, 0, 0, 0);
     }
-    const float biasl2 = *reinterpret_cast<const float*>(gb + bias_off) * sl2;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (ah[r] + al[r]) * sl2 + biasl2;
+    for (int r = 0; r < 4; ++r) sc[r] = (ah[r] + al[r]) * sl2 + bias_l2;
 }
 
-// Write the 4 waves' states to LDS: m, l per (wave, head) and
-// o = O + sum_t p_t zero_t per (wave, head, channel). Every thread calls it.
-template <int NG, int NB, bool kValueOffset>
-__device__ __forceinline__ void stash_waves(Acc<NG, NB>& st, uint8_t* smem) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, j = lane >> 4;
-    const float l_tot = xor_sum(st.l_acc);
-    float zt[NG][NB];
+// Value side of a main tile: W = p * scale (hi, lo) per channel group and
+// pair-factor variant, zero-points through zacc, one MFMA per channel tile.
+template <int BITS, int NG, int NB>
+__device__ __forceinline__ void value_tile(Acc<NG, NB>& st, const uint32_t* vw, const uint32_t* vm, const float p[4]) {
+    h8 Bv[NG][NB];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-        const float z = xor_sum(st.zacc[gg]);
-#pragma unroll
-        for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - (kValueOffset ? 1024.0f * xor_sum(st.wsum[gg][vb]) : 0.0f);
-    }
-    __syncthreads();  // LDS tables no longer read
-    float* sm_m = reinterpret_cast<float*>(smem);  // [kWaves][16]
-    float* sm_l = sm_m + kWaves * 16;              // [kWaves][16]
-    float* sm_o = sm_l + kWaves * 16;              // [kWaves][16][128]
-    if (j == 0) {
-        sm_m[wave * 16 + n] = st.m_run;
-        sm_l[wave * 16 + n] = l_tot;
-    }
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
+        float Sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int chn = 16 * tt + 4 * j + r;
-            sm_o[(wave * 16 + n) * kHeadDim + chn] = st.O[tt][r] + zt[chn / (kHeadDim / NG)][tt % NB];
+            const uint32_t mw = vm[r * NG + gg];
+            Sv[r] = f16_bits_to_f32((uint16_t)(mw & 0xFFFFu));
+            st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
         }
-    __syncthreads();
+#pragma unroll
+        for (int vb = 0; vb < NB; ++vb) {
+            float ws = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float wv = p[r] * Sv[r] * v_inv_factor<BITS>(vb, r);
+                _Float16 hi, lo;
+                split_f16(wv, hi, lo);
+                Bv[gg][vb][r] = hi;
+                Bv[gg][vb][4 + r] = lo;
+                ws += wv;
+            }
+            st.wsum[gg][vb] += ws;
+        }
+    }
+    h4 Av[8];
+    unpack_v<BITS>(vw, Av);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const int gg = (16 * tt) / (kHeadDim / NG);
+        st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(Av[tt]), Bv[gg][tt % NB], st.O[tt], 0, 0, 0);
+    }
 }
 
-// One work group per (sequence, KV head, split). Splits cover the "main"
-// 16-token tiles, whose Keys and Values are both quantised; the last split
-// of a sequence also covers the tail tiles that touch the residual. Each
-// wave takes a contiguous tile range with one buffer of tiles in flight
-// while it computes the other. Every split writes a partial (m, l, o); the
-// last work group of a (sequence, KV head) to finish merges them:
+template <int BITS, int NG>
+struct TileRegs {
+    uint32_t k[BITS];
+    uint32_t v[BITS];
+    uint32_t vm[4 * NG];
+};
+
+// Loads of one tail tile (a tile that touches the residual): Keys from codes
+// (t < TK / 16) or from the fp16 residual, Value tokens from codes (< TV) or
+// the residual.
+template <int BITS, int NG>
+struct TailRegs {
+    uint32_t kw[BITS], vw[BITS], vm[4 * NG];
+    uint4 kr[4];
+    uint2 vr[8];
+    uint4 ms, mz;
+    int blk;
+};
+
+// One work group (4 waves) per (sequence, KV head, split). The main tiles
+// (Key and Value both quantised) of a (sequence, KV head) are cut into
+// 4 x n_valid contiguous wave ranges; the tail tiles (touching the residual)
+// are dealt out one per wave. Each wave streams its range on its own: page
+// ids of a 64-tile window, one buffer of tiles in flight while the other is
+// computed, and the query table of each Key group built in its own LDS rows
+// when the group begins (scales and zero-points travel with the tile loads).
+// The 4 waves merge in LDS into one partial (m, l, o) per query head; the
+// last work group of a (sequence, KV head) to finish merges the partials:
 // m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
 template <int BITS, int DT, int NG>
-__global__ __launch_bounds__(kThreads, (NG == 1 ? 3 : 2)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+    constexpr int kHalf = buffer_tiles<NG>();
     constexpr int TILE_BYTES = kTile * kHeadDim * BITS / 8;
     constexpr int SLOT_BYTES = 4 * BITS;
     constexpr int NB = (BITS == 2) ? 2 : 1;  // Value pair-factor variants
@@ -582,12 +506,9 @@ __global__ __launch_bounds__(kThreads, (NG == 1 ? 3 : 2)) void decode_kernel(Dec
     const int split = blockIdx.x % a.n_splits;
     const int sh = blockIdx.x / a.n_splits;
     const WgCtx c = make_ctx(a, sh / H, sh % H);
-    const int tps = a.tiles_per_split;
-    const int nvalid = c.n_main > 0 ? min(a.n_splits, (c.n_main + tps - 1) / tps) : 1;
+    // at least kMinSplitTiles main tiles per split when there are that many
+    const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
     if (split >= nvalid) return;
-    const bool last = split == nvalid - 1;
-    const int t_begin = split * tps;
-    const int t_end = last ? c.n_main : t_begin + tps;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, j = lane >> 4;
@@ -595,298 +516,317 @@ __global__ __launch_bounds__(kThreads, (NG == 1 ? 3 : 2)) void decode_kernel(Dec
     const int R = V.R;
     const int T = c.T, TV = c.TV;
     const int tk_tiles = c.TK / kTile;
+    const int tpg = 1 << a.tpg_shift, tpp = 1 << a.tpp_shift;
+    const int nch = kHeadDim * V.Bk / V.G;  // Key channels whose meta one page holds
+    const int meta_tile = (8 * (lane & 15) / nch) * tpp;  // tile (in its group) whose page holds this lane's meta
     const float sl2 = a.scale_log2;
     const int HQ = a.num_q_heads;
 
-    uint16_t* lds_zero = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* lds_q = lds_zero + kQRow;
-    uint8_t* lds_groups = smem + head_lds_bytes(g);
-    const int gbytes = group_lds_bytes(g);
-    {
-        QueryLoads ql;
-        query_load<DT>(a, c, ql);
-        query_store<DT>(c, ql, lds_zero);
-    }
-    const int nr = n < g ? n : n % g;
+    const int nslots = kWaves * nvalid;
+    const int wslot = split * kWaves + wave;  // main range: contiguous in split-major order
+    const int m_begin = (int)(((long long)wslot * c.n_main) / nslots);
+    const int m_end = (int)(((long long)(wslot + 1) * c.n_main) / nslots);
+    const int n_tail = (T + kTile - 1) / kTile - c.n_main;
+    const int tail_rank = wave * nvalid + split;  // tail tiles: rank, rank + nslots, ...
+    const int my_tail = n_tail > tail_rank ? (n_tail - tail_rank + nslots - 1) / nslots : 0;
+
+    uint8_t* wl = smem + wave * wave_lds_bytes(g);
+    uint16_t* lq = reinterpret_cast<uint16_t*>(wl);
+    uint8_t* lt = wl + g * kRowBytes;
+    float* lbias = reinterpret_cast<float*>(lt + 2 * g * kRowBytes);
+    const int nr = n < g ? n : n % g;  // padding lanes mirror a real head; their results are unused
     const int lane_row = nr * 2 * kRowBytes + 16 * j;
-    const int lane_bias = g * 2 * kRowBytes + 256 + 4 * nr;
     const uint32_t lane_code_off = SLOT_BYTES * lane;
     const uint32_t lane_meta_off = 16 * NG * j;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(V.k_codes, a.code_array_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V.v_codes, a.code_array_bytes);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(V.v_meta, a.vmeta_array_bytes);
+    const __amdgpu_buffer_rsrc_t rkm = make_rsrc(V.k_meta, a.kmeta_array_bytes);
     const uint16_t* ringK = V.k_ring + ((size_t)max(c.slot, 0) * H + c.h) * V.ring_elems;
     const uint16_t* ringV = V.v_ring + ((size_t)max(c.slot, 0) * H + c.h) * V.ring_elems;
 
+    // ---- first round trip: query rows, page ids of the first two windows
+    // and of the first tail tile's Key group ----
+    const int base0 = (m_begin >> a.tpg_shift) << a.tpg_shift;  // windows start on a group
+    int my_page = page_of_tile(a, c, base0 + lane);
+    int next_page = page_of_tile(a, c, base0 + 64 + lane);
+    const int tail0 = c.n_main + tail_rank;
+    const int tail_base0 = (tail0 >> a.tpg_shift) << a.tpg_shift;
+    int tail_page = my_tail > 0 ? page_of_tile(a, c, tail_base0 + lane) : -1;
+    load_query<DT>(a, c, lq);
+
     Acc<NG, NB> st;
     st.init();
-    const int chunk_tiles = max(1, (a.lds_groups - 1) << a.tpg_shift);
 
-    // ---------------- main tiles ----------------
-    for (int c0 = t_begin; c0 < t_end; c0 += chunk_tiles) {
-        const int c1 = min(t_end, c0 + chunk_tiles);
-        const int g_first = c0 >> a.tpg_shift;
-        const int n_groups = ((c1 - 1) >> a.tpg_shift) - g_first + 1;
-        const int nt = c1 - c0;
-        const int per_wave = (nt + kWaves - 1) / kWaves;
-        const int w_begin = c0 + wave * per_wave;
-        const int w_end = min(c1, w_begin + per_wave);
-        int my_page = (w_begin + lane < w_end) ? page_of_tile(a, c, w_begin + lane) : -1;
-        // Loads of a tile are unconditional (a missing page or a tile past
-        // the range reads page 0 and is not computed), so a buffer of tiles
-        // is one straight run of loads that the wait counts can follow.
-        // Offsets: scalar per tile, per lane fixed.
-        auto issue = [&](int t, TileRegs<BITS, NG>& r) -> bool {
-            const int blk = __builtin_amdgcn_readlane(my_page, (t - w_begin) & 63);
-            const bool valid = blk >= 0 && t < w_end;
-            const uint32_t chk = (uint32_t)(valid ? blk : 0) * (uint32_t)H + (uint32_t)c.h;
+    // ---- tail tiles ----
+    auto tail_issue = [&](int t, int tpage, TailRegs<BITS, NG>& x) {
+        const int tb = (t >> a.tpg_shift) << a.tpg_shift;
+        x.blk = __builtin_amdgcn_readlane(tpage, t - tb);
+        const int blk = max(x.blk, 0);
+        const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)c.h;
+        const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
+        const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
+        const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
+        const int p0 = t * kTile;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) x.kw[k] = x.vw[k] = 0;
+#pragma unroll
+        for (int k = 0; k < 4 * NG; ++k) x.vm[k] = 0;
+        x.ms = x.mz = (uint4){0, 0, 0, 0};
+        if (t < tk_tiles) {
+            if constexpr (BITS == 4) {
+                const uint4 u = buf_b128(rk, lane_code_off, coff);
+                x.kw[0] = u.x; x.kw[1] = u.y; x.kw[2] = u.z; x.kw[3] = u.w;
+            } else {
+                const uint2 u = buf_b64(rk, lane_code_off, coff);
+                x.kw[0] = u.x; x.kw[1] = u.y;
+            }
+            const int mp = __builtin_amdgcn_ds_bpermute(4 * meta_tile, tpage);
+            const uint32_t mo = k_meta_off(V, c.h, mp, nch);
+            x.ms = buf_b128(rkm, mo, 0);
+            x.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+        } else {
+            const int pk = min(p0 + n, T - 1);  // A row: token n of the tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x.kr[i] = *reinterpret_cast<const uint4*>(ringK + (size_t)(pk % R) * kHeadDim + 32 * i + 8 * j);
+        }
+        if (p0 < TV) {
+            if constexpr (BITS == 4) {
+                const uint4 u = buf_b128(rv, lane_code_off, coff);
+                x.vw[0] = u.x; x.vw[1] = u.y; x.vw[2] = u.z; x.vw[3] = u.w;
+            } else {
+                const uint2 u = buf_b64(rv, lane_code_off, coff);
+                x.vw[0] = u.x; x.vw[1] = u.y;
+            }
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                const uint4 m = buf_b128(rm, lane_meta_off + 16 * q, moff);
+                x.vm[4 * q + 0] = m.x; x.vm[4 * q + 1] = m.y; x.vm[4 * q + 2] = m.z; x.vm[4 * q + 3] = m.w;
+            }
+        }
+        // residual Values: positions 4j..4j+3 of a channel are adjacent in the
+        // channel-major ring (R is a multiple of 16, so they never wrap)
+        const int pq = p0 + 4 * j;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+            x.vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
+    };
+    auto tail_compute = [&](int t, const TailRegs<BITS, NG>& x) {
+        if (x.blk < 0) return;
+        const int p0 = t * kTile, pq = p0 + 4 * j;
+        float sc[4];
+        if (t < tk_tiles) {
+            const float bias_l2 = build_table<BITS>(g, x.ms, x.mz, lq, lt, lbias, nr, sl2);
+            code_scores<BITS>(x.kw, lt, lane_row, bias_l2, sl2, sc);
+        } else {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            const uint8_t* qrow = reinterpret_cast<const uint8_t*>(lq + nr * kQRow);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h8 A;
+                const uint32_t ws[4] = {x.kr[i].x, x.kr[i].y, x.kr[i].z, x.kr[i].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) A[e] = (_Float16)to_f32<DT>((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+                const h8 B = *reinterpret_cast<const h8*>(qrow + 2 * (32 * i + 8 * j));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = (p0 + 4 * j + r < T) ? acc[r] * sl2 : -INFINITY;
+        }
+        float p[4];
+        st.update(sc, p);
+        // Value token r: code (< TV), residual (< T) or masked, chosen by
+        // selects (no divergent branches)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const int gg = (16 * tt) / (kHeadDim / NG);
+            const bool first_of_group = (16 * tt) % (kHeadDim / NG) == 0;
+            const uint32_t rw[2] = {x.vr[tt].x, x.vr[tt].y};
+            h4 A;
+            h8 B;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pr = pq + r;
+                const bool is_code = pr < TV, is_raw = !is_code && pr < T;
+                const uint32_t mw = is_code ? x.vm[r * NG + gg] : 0u;
+                if (first_of_group) st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
+                const float code_v = (float)v_code_at<BITS>(x.vw, tt, r);
+                const float raw_v = to_f32<DT>((uint16_t)(rw[r >> 1] >> (16 * (r & 1))));
+                const float av = is_code ? code_v : (is_raw ? raw_v : 0.0f);
+                const float wv = is_code ? p[r] * f16_bits_to_f32((uint16_t)(mw & 0xFFFFu)) : (is_raw ? p[r] : 0.0f);
+                A[r] = (_Float16)av;
+                _Float16 hi, lo;
+                split_f16(wv, hi, lo);
+                B[r] = hi;
+                B[4 + r] = lo;
+            }
+            st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, st.O[tt], 0, 0, 0);
+        }
+    };
+
+    // ---- main tiles ----
+    // Loads of a tile are unconditional (a missing page or a tile past the
+    // range reads page 0 and is not computed), so a buffer is one straight
+    // run of loads that the wait counts can follow. Each buffer also loads
+    // the scales and zero-points of the Key group of its last tile: the only
+    // group that can begin inside a buffer when groups span >= kHalf tiles
+    // (other group starts load theirs when they are reached).
+    struct Buf {
+        TileRegs<BITS, NG> t[kHalf];
+        bool ok[kHalf];
+        uint4 ms, mz;
+    };
+    int base = base0;
+    auto issue = [&](int t0, Buf& b) {
+        if (t0 - base >= 64) {  // next window of page ids (loaded one window ahead)
+            base += 64;
+            my_page = next_page;
+            next_page = page_of_tile(a, c, base + 64 + lane);
+        }
+#pragma unroll
+        for (int e = 0; e < kHalf; ++e) {
+            const int t = t0 + e;
+            const int blk = __builtin_amdgcn_readlane(my_page, (t - base) & 63);
+            b.ok[e] = blk >= 0 && t >= m_begin && t < m_end;
+            const uint32_t chk = (uint32_t)(b.ok[e] ? blk : 0) * (uint32_t)H + (uint32_t)c.h;
             const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
             const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
             const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
             if constexpr (BITS == 4) {
                 const uint4 k4 = buf_b128(rk, lane_code_off, coff);
                 const uint4 v4 = buf_b128(rv, lane_code_off, coff);
-                r.k[0] = k4.x; r.k[1] = k4.y; r.k[2] = k4.z; r.k[3] = k4.w;
-                r.v[0] = v4.x; r.v[1] = v4.y; r.v[2] = v4.z; r.v[3] = v4.w;
+                b.t[e].k[0] = k4.x; b.t[e].k[1] = k4.y; b.t[e].k[2] = k4.z; b.t[e].k[3] = k4.w;
+                b.t[e].v[0] = v4.x; b.t[e].v[1] = v4.y; b.t[e].v[2] = v4.z; b.t[e].v[3] = v4.w;
             } else {
                 const uint2 k2 = buf_b64(rk, lane_code_off, coff);
                 const uint2 v2 = buf_b64(rv, lane_code_off, coff);
-                r.k[0] = k2.x; r.k[1] = k2.y;
-                r.v[0] = v2.x; r.v[1] = v2.y;
+                b.t[e].k[0] = k2.x; b.t[e].k[1] = k2.y;
+                b.t[e].v[0] = v2.x; b.t[e].v[1] = v2.y;
             }
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
                 const uint4 m = buf_b128(rm, lane_meta_off + 16 * q, moff);
-                r.vm[4 * q + 0] = m.x; r.vm[4 * q + 1] = m.y; r.vm[4 * q + 2] = m.z; r.vm[4 * q + 3] = m.w;
+                b.t[e].vm[4 * q + 0] = m.x; b.t[e].vm[4 * q + 1] = m.y;
+                b.t[e].vm[4 * q + 2] = m.z; b.t[e].vm[4 * q + 3] = m.w;
             }
-            return valid;
-        };
-        auto compute = [&](const TileRegs<BITS, NG>& cur, int t) {
-            const uint8_t* gb = lds_groups + ((t >> a.tpg_shift) - g_first) * gbytes;
+        }
+        // Key group of tile t0 + kHalf - 1 (its pages are in the window:
+        // windows start on groups)
+        const int gt = ((t0 + kHalf - 1) >> a.tpg_shift) << a.tpg_shift;
+        const int mp = __builtin_amdgcn_ds_bpermute(4 * ((gt + meta_tile - base) & 63), my_page);
+        const uint32_t mo = k_meta_off(V, c.h, mp, nch);
+        b.ms = buf_b128(rkm, mo, 0);
+        b.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+    };
+    float bias_l2 = 0.0f;
+    auto compute = [&](const Buf& b, int t0) {
+#pragma unroll
+        for (int e = 0; e < kHalf; ++e) {
+            const int t = t0 + e;
+            if (!b.ok[e]) continue;
+            if ((t & (tpg - 1)) == 0 && t != m_begin) {
+                uint4 ms = b.ms, mz = b.mz;
+                if (e + tpg < kHalf) {  // short groups: this group's meta is not in the buffer
+                    const int mp = __builtin_amdgcn_ds_bpermute(4 * ((t + meta_tile - base) & 63), my_page);
+                    const uint32_t mo = k_meta_off(V, c.h, mp, nch);
+                    ms = buf_b128(rkm, mo, 0);
+                    mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+                }
+                bias_l2 = build_table<BITS>(g, ms, mz, lq, lt, lbias, nr, sl2);
+            }
             float sc[4], p[4];
-            code_scores_lds<BITS>(cur.k, gb, lane_row, lane_bias, sl2, sc);
+            code_scores<BITS>(b.t[e].k, lt, lane_row, bias_l2, sl2, sc);
             st.update(sc, p);
-            // Value side: W = p * scale (hi, lo) per channel group and pair-factor variant
-            h8 Bv[NG][NB];
-#pragma unroll
-            for (int gg = 0; gg < NG; ++gg) {
-                float Sv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t mw = cur.vm[r * NG + gg];
-                    Sv[r] = f16_bits_to_f32((uint16_t)(mw & 0xFFFFu));
-                    st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
-                }
-#pragma unroll
-                for (int vb = 0; vb < NB; ++vb) {
-                    float ws = 0.0f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float wv = p[r] * Sv[r] * v_inv_factor<BITS>(vb, r);
-                        _Float16 hi, lo;
-                        split_f16(wv, hi, lo);
-                        Bv[gg][vb][r] = hi;
-                        Bv[gg][vb][4 + r] = lo;
-                        ws += wv;
-                    }
-                    st.wsum[gg][vb] += ws;
-                }
+            value_tile<BITS, NG, NB>(st, b.t[e].v, b.t[e].vm, p);
+        }
+    };
+
+    // ---- second round trip: first main buffer, the first group's meta and
+    // the first tail tile, all in flight together (narrow Value groups, whose
+    // tiles hold many registers, finish the tail first) ----
+    auto run_tail = [&]() {
+        for (int i = 0; i < my_tail; ++i) {
+            const int t = tail0 + i * nslots;
+            if (i > 0) {
+                const int tb = (t >> a.tpg_shift) << a.tpg_shift;
+                tail_page = page_of_tile(a, c, tb + lane);
             }
-            h4 Av[8];
-            unpack_v<BITS>(cur.v, Av);
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const int gg = (16 * tt) / (kHeadDim / NG);
-                st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(Av[tt]), Bv[gg][tt % NB], st.O[tt], 0, 0, 0);
-            }
-        };
-        TableLoads tl;
-        table_pages(a, c, n_groups, [&](int k) { return g_first + k; }, tl);
-        table_meta(a, c, tl);
-        __syncthreads();  // query rows stored; previous chunk's tables no longer read
-        table_fill<BITS>(c, n_groups, tl, lds_q, lds_groups);
-        // two buffers of kHalf tiles: one buffer's loads are in flight while
-        // the other's tiles are computed
-        TileRegs<BITS, NG> ra[kHalf], rb[kHalf];
-        bool oka[kHalf], okb[kHalf];
-        auto issue_half = [&](int t, TileRegs<BITS, NG>* r, bool* ok) {
-            if (((t - w_begin) & 63) == 0 && t != w_begin)
-                my_page = (t + lane < w_end) ? page_of_tile(a, c, t + lane) : -1;
-#pragma unroll
-            for (int b = 0; b < kHalf; ++b) ok[b] = issue(t + b, r[b]);
-        };
-        auto compute_half = [&](int t, const TileRegs<BITS, NG>* r, const bool* ok) {
-#pragma unroll
-            for (int b = 0; b < kHalf; ++b)
-                if (ok[b]) compute(r[b], t + b);
-        };
-        issue_half(w_begin, ra, oka);
-        for (int t0 = w_begin; t0 < w_end; t0 += 2 * kHalf) {
-            issue_half(t0 + kHalf, rb, okb);
-            compute_half(t0, ra, oka);
-            if (t0 + kHalf >= w_end) break;
-            issue_half(t0 + 2 * kHalf, ra, oka);
-            compute_half(t0 + kHalf, rb, okb);
+            TailRegs<BITS, NG> x;
+            tail_issue(t, tail_page, x);
+            tail_compute(t, x);
+        }
+    };
+    if constexpr (NG >= 4) run_tail();
+    // buffers start a multiple of kHalf tiles after the window base, so
+    // window boundaries fall between buffers (tiles before m_begin may ride
+    // along, not computed)
+    const int t_first = m_begin - ((m_begin - base0) & (kHalf - 1));
+    Buf ba, bb;
+    uint4 ms0 = {0, 0, 0, 0}, mz0 = {0, 0, 0, 0};
+    if (m_begin < m_end) {
+        issue(t_first, ba);
+        const int mp = __builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page);
+        const uint32_t mo = k_meta_off(V, c.h, mp, nch);
+        ms0 = buf_b128(rkm, mo, 0);
+        mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+    }
+    if constexpr (NG < 4) run_tail();
+    if (m_begin < m_end) {
+        bias_l2 = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sl2);
+        for (int t0 = t_first; t0 < m_end; t0 += 2 * kHalf) {
+            issue(t0 + kHalf, bb);
+            compute(ba, t0);
+            if (t0 + kHalf >= m_end) break;
+            issue(t0 + 2 * kHalf, ba);
+            compute(bb, t0 + kHalf);
         }
     }
 
-    // ---------------- tail tiles ----------------
-    // Tiles that touch the residual (Keys from codes or the residual; each
-    // Value token from codes (< TV), the residual (< T) or masked) are dealt
-    // out over the valid splits: split i takes tail tiles i, i + nvalid, ...,
-    // one per wave per round.
-    const int n_tail = (T + kTile - 1) / kTile - c.n_main;
-    const int my_tail = n_tail > split ? (n_tail - split + nvalid - 1) / nvalid : 0;
-    for (int r0 = 0; r0 < my_tail; r0 += kWaves) {
-        // this round's tiles: k = r0 .. r0+3 of this split's list; the Key groups
-        // of code tiles get one table slot per wave
-        __syncthreads();
-        int gsel[kWaves];  // table slot w: Key group of wave w's tile, or none
+    // ---------------- merge the 4 waves in LDS ----------------
+    {
+        const float l_tot = xor_sum(st.l_acc);
+        float zt[NG][NB];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const int kq = r0 + w;
-            const int tw = c.n_main + split + kq * nvalid;
-            gsel[w] = (kq < my_tail && tw < tk_tiles) ? (tw >> a.tpg_shift) : -1;
+        for (int gg = 0; gg < NG; ++gg) {
+            const float z = xor_sum(st.zacc[gg]);
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - (BITS == 4 ? 1024.0f * xor_sum(st.wsum[gg][vb]) : 0.0f);
         }
-        TableLoads tl;
-        table_pages(a, c, kWaves, [&](int k) { return gsel[k]; }, tl);
-        table_meta(a, c, tl);
-        table_fill<BITS>(c, kWaves, tl, lds_q, lds_groups);
-        const int kq = r0 + wave;
-        const int w_begin = c.n_main + split + kq * nvalid;
-        const int w_end = kq < my_tail ? w_begin + 1 : w_begin;
-        for (int t = w_begin; t < w_end; ++t) {
-            const int p0 = t * kTile;
-            const int blk = page_of_tile(a, c, t);
-            if (blk < 0) continue;
-            const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)c.h;
-            const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
-            const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
-            const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
-            const bool kcode = t < tk_tiles;
-            const bool vcode = p0 < TV;
-            // ---- every load of the tile first ----
-            uint32_t kw[BITS], vw[BITS], vm[4 * NG];
-            uint4 kr[4];
-            uint2 vr[8];
-#pragma unroll
-            for (int k = 0; k < BITS; ++k) kw[k] = vw[k] = 0;
-#pragma unroll
-            for (int k = 0; k < 4 * NG; ++k) vm[k] = 0;
-            if (kcode) {
-                if constexpr (BITS == 4) {
-                    const uint4 u = buf_b128(rk, lane_code_off, coff);
-                    kw[0] = u.x; kw[1] = u.y; kw[2] = u.z; kw[3] = u.w;
-                } else {
-                    const uint2 u = buf_b64(rk, lane_code_off, coff);
-                    kw[0] = u.x; kw[1] = u.y;
-                }
-            } else {
-                const int pk = min(p0 + n, T - 1);  // A row: token n of the tile
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    kr[i] = *reinterpret_cast<const uint4*>(ringK + (size_t)(pk % R) * kHeadDim + 32 * i + 8 * j);
+        __syncthreads();  // every wave is done with its LDS rows
+        float* sm_m = reinterpret_cast<float*>(smem);  // [kWaves][g]
+        float* sm_l = sm_m + kWaves * g;               // [kWaves][g]
+        float* sm_o = sm_l + kWaves * g;               // [kWaves][g][128]
+        if (n < g) {
+            if (j == 0) {
+                sm_m[wave * g + n] = st.m_run;
+                sm_l[wave * g + n] = l_tot;
             }
-            if (vcode) {
-                if constexpr (BITS == 4) {
-                    const uint4 u = buf_b128(rv, lane_code_off, coff);
-                    vw[0] = u.x; vw[1] = u.y; vw[2] = u.z; vw[3] = u.w;
-                } else {
-                    const uint2 u = buf_b64(rv, lane_code_off, coff);
-                    vw[0] = u.x; vw[1] = u.y;
-                }
-#pragma unroll
-                for (int q = 0; q < NG; ++q) {
-                    const uint4 m = buf_b128(rm, lane_meta_off + 16 * q, moff);
-                    vm[4 * q + 0] = m.x; vm[4 * q + 1] = m.y; vm[4 * q + 2] = m.z; vm[4 * q + 3] = m.w;
-                }
-            }
-            // residual Values: positions 4j..4j+3 of a channel are adjacent in the
-            // channel-major ring (R is a multiple of 16, so they never wrap)
-            const int pq = p0 + 4 * j;
 #pragma unroll
             for (int tt = 0; tt < 8; ++tt)
-                vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
-
-            // ---- scores ----
-            float sc[4];
-            if (kcode) {
-                const uint8_t* gb = lds_groups + wave * gbytes;
-                code_scores_lds<BITS>(kw, gb, lane_row, lane_bias, sl2, sc);
-            } else {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                const uint8_t* qrow = reinterpret_cast<const uint8_t*>(lds_q + nr * kQRow);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h8 A;
-                    const uint32_t ws[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) A[e] = (_Float16)to_f32<DT>((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
-                    const h8 B = *reinterpret_cast<const h8*>(qrow + 2 * (32 * i + 8 * j));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[r] = (p0 + 4 * j + r < T) ? acc[r] * sl2 : -INFINITY;
-            }
-            float p[4];
-            st.update(sc, p);
-            // ---- values ----
-            float Sv[4][NG];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool code_tok = pq + r < TV;
-#pragma unroll
-                for (int gg = 0; gg < NG; ++gg) {
-                    const uint32_t mw = code_tok ? vm[r * NG + gg] : 0u;
-                    Sv[r][gg] = f16_bits_to_f32((uint16_t)(mw & 0xFFFFu));
-                    st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const int gg = (16 * tt) / (kHeadDim / NG);
-                const uint32_t rw[2] = {vr[tt].x, vr[tt].y};
-                h4 A;
-                h8 B;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int pr = pq + r;
-                    float av = 0.0f, wv = 0.0f;
-                    if (pr < TV) {
-                        av = (float)v_code_at<BITS>(vw, tt, r);
-                        wv = p[r] * Sv[r][gg];
-                    } else if (pr < T) {
-                        av = to_f32<DT>((uint16_t)(rw[r >> 1] >> (16 * (r & 1))));
-                        wv = p[r];
-                    }
-                    A[r] = (_Float16)av;
-                    _Float16 hi, lo;
-                    split_f16(wv, hi, lo);
-                    B[r] = hi;
-                    B[4 + r] = lo;
+                    const int chn = 16 * tt + 4 * j + r;
+                    sm_o[(wave * g + n) * kHeadDim + chn] = st.O[tt][r] + zt[chn / (kHeadDim / NG)][tt % NB];
                 }
-                st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, st.O[tt], 0, 0, 0);
-            }
         }
+        __syncthreads();
     }
-
-    // ---------------- this split's partial ----------------
-    stash_waves<NG, NB, BITS == 4>(st, smem);
     const float* sm_m = reinterpret_cast<const float*>(smem);
-    const float* sm_l = sm_m + kWaves * 16;
-    const float* sm_o = sm_l + kWaves * 16;
+    const float* sm_l = sm_m + kWaves * g;
+    const float* sm_o = sm_l + kWaves * g;
     for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
         const int hn = idx / kHeadDim, chn = idx % kHeadDim;
         float mstar = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm_m[w * 16 + hn]);
+        for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm_m[w * g + hn]);
         float lsum = 0.0f, osum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = sm_m[w * 16 + hn];
+            const float mw = sm_m[w * g + hn];
             const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - mstar);
-            lsum += f * sm_l[w * 16 + hn];
-            osum += f * sm_o[(w * 16 + hn) * kHeadDim + chn];
+            lsum += f * sm_l[w * g + hn];
+            osum += f * sm_o[(w * g + hn) * kHeadDim + chn];
         }
         float* part = a.partials + (((size_t)c.s * HQ + c.h * g + hn) * a.n_splits + split) * kPartialStride;
         if (chn == 0) {
@@ -911,13 +851,13 @@ __global__ __launch_bounds__(kThreads, (NG == 1 ? 3 : 2)) void decode_kernel(Dec
     for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
         const int hn = idx / kHeadDim, chn = idx % kHeadDim;
         const int hq = c.h * g + hn;
-        const float* base = a.partials + ((size_t)c.s * HQ + hq) * a.n_splits * kPartialStride;
+        const float* pbase = a.partials + ((size_t)c.s * HQ + hq) * a.n_splits * kPartialStride;
         float mstar = -INFINITY;
-        for (int i = 0; i < nvalid; ++i) mstar = fmaxf(mstar, base[(size_t)i * kPartialStride]);
+        for (int i = 0; i < nvalid; ++i) mstar = fmaxf(mstar, pbase[(size_t)i * kPartialStride]);
         float lsum = 0.0f, osum = 0.0f;
         if (mstar != -INFINITY) {
             for (int i = 0; i < nvalid; ++i) {
-                const float* pp = base + (size_t)i * kPartialStride;
+                const float* pp = pbase + (size_t)i * kPartialStride;
                 const float mi = pp[0];
                 if (mi == -INFINITY) continue;
                 const float f = __builtin_amdgcn_exp2f(mi - mstar);
@@ -960,12 +900,11 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     a.counters = reinterpret_cast<int*>(partials);
     a.partials = partials + plan.counter_floats;
     a.n_splits = plan.n_splits;
-    a.tiles_per_split = plan.tiles_per_split;
-    a.lds_groups = plan.lds_groups;
     a.tpg_shift = __builtin_ctz((unsigned)(v.G / kTile));
     a.tpp_shift = __builtin_ctz((unsigned)(v.Bk / kTile));
     a.code_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.code_bytes);
     a.vmeta_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.v_meta_bytes);
+    a.kmeta_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.k_meta_bytes);
     a.out = static_cast<uint16_t*>(out);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int ng = kHeadDim / v.Gv;
@@ -981,13 +920,8 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     return (int)hipGetLastError();
 }
 
-// LDS budget of one decode work group (three work groups per compute unit).
-int decode_lds_groups(int g) {
-    const int budget = 52 * 1024;
-    return std::min(kTableRounds * kThreads / 16, std::max(kWaves, (budget - head_lds_bytes(g)) / group_lds_bytes(g)));
-}
-size_t decode_lds_bytes(int g, int groups) {
-    return std::max((size_t)kMergeBytes, (size_t)head_lds_bytes(g) + (size_t)groups * group_lds_bytes(g));
+size_t decode_lds_bytes(int g) {
+    return std::max((size_t)kWaves * wave_lds_bytes(g), (size_t)merge_lds_bytes(g));
 }
 
 }  // namespace kivi

@@ -32,21 +32,19 @@ struct CacheView {
 
 CacheView view_of(const kivi_cache* c);
 
-// Split plan for decode: main tiles of a sequence are cut into splits of
-// `tiles_per_split`; the last split of a sequence also takes the tail (tiles
-// that touch the residual). The workspace holds one merge counter per
+// Split plan for decode: the grid has n_splits work groups per (sequence,
+// KV head); a sequence uses min(n_splits, ceil(main tiles / kMinSplitTiles))
+// of them (at least one). The workspace holds one merge counter per
 // (sequence, KV head), then the partials.
+constexpr int kMinSplitTiles = 32;
 struct DecodePlan {
     int n_splits;
-    int tiles_per_split;
-    int lds_groups;     // Key-group query tables held in LDS at once
     size_t lds_bytes;   // dynamic LDS of one decode work group
     size_t counter_floats;  // leading workspace words holding the merge counters
     size_t ws_bytes;
 };
 DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len);
-int decode_lds_groups(int gqa);
-size_t decode_lds_bytes(int gqa, int groups);
+size_t decode_lds_bytes(int gqa);
 
 constexpr int kPartialStride = 132;  // floats per partial: m, l, pad, pad, o[128]
 
