@@ -158,7 +158,7 @@ def main():
     lens = [np.full(S, T0, dtype=np.int64) for _ in range(n_rep)]
     max_len = T0 + steps_per_rep + 1
     ws_bytes = kivi.kivi_decode_workspace_bytes(handles[0], S, HQ, max_len)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # merge counters start at zero
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)  # split partials, if any
     out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
     # per-step length tensors, prepared up front so the timed loop launches only library work
     lens_before_dev = [torch.from_numpy(np.full(S, T0 + i // n_rep, np.int32)).to(dev) for i in range(total)]

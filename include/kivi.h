@@ -181,10 +181,10 @@ kivi_status kivi_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_
                                int32_t max_new, const void* d_k_new, const void* d_v_new,
                                const int32_t* d_block_table, int32_t bt_stride, void* stream);
 
-/* Workspace bytes kivi_decode_attention needs for these sizes. The
- * workspace starts with one counter per (sequence, KV head) that merges the
- * splits: it must be zero-filled before its first use, and every call
- * leaves it zero-filled again. Calls that share a workspace must not
+/* Workspace bytes kivi_decode_attention needs for these sizes (0 when no
+ * sequence is split across work groups). The workspace holds the per-split
+ * partial results between the attention kernel and the merge kernel of one
+ * call; it needs no initialisation. Calls that share a workspace must not
  * overlap on the device.                                                    */
 kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
                                         int32_t num_q_heads, int32_t max_seq_len, size_t* bytes);
@@ -198,7 +198,7 @@ kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seq
  *   softmax_scale       multiplies q.k (1/sqrt(128) for standard attention)
  *   d_out[S][H_Q][128]  kv_dtype; a sequence of length 0 gets zeros
  *   d_ws, ws_bytes      device workspace of kivi_decode_workspace_bytes()
- *                       (zero-filled before first use; see above)
+ *                       bytes (may be NULL when that is 0)
  * H_Q must be a multiple of H_KV with H_Q/H_KV <= 16 (else UNSUPPORTED).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
 kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,

@@ -141,17 +141,16 @@ DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int m
     const int gqa = std::max(1, std::min(kMaxGqa, num_q_heads / H));
     const int main_tiles = std::max(0, max_seq_len - R) / kTile;
     const int pairs = std::max(1, num_seqs * H);
-    // one round of resident work groups (256 CUs x 2), at least
-    // kMinSplitTiles main tiles per split
-    const int resident = 2 * 256;
+    // one round of resident work groups (one 8-wave work group per CU on
+    // 256 CUs), at least kMinSplitTiles main tiles per split
+    const int resident = 256;
     int n_splits = std::max(1, (resident + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (main_tiles + kMinSplitTiles - 1) / kMinSplitTiles));
     n_splits = std::max(1, std::min(n_splits, 256));
     DecodePlan p;
     p.n_splits = n_splits;
     p.lds_bytes = decode_lds_bytes(gqa);
-    p.counter_floats = (((size_t)num_seqs * H + 63) / 64) * 64;  // 256-byte aligned
-    p.ws_bytes = (p.counter_floats + (size_t)num_seqs * num_q_heads * n_splits * kPartialStride) * sizeof(float);
+    p.ws_bytes = n_splits > 1 ? (size_t)num_seqs * num_q_heads * n_splits * kPartialStride * sizeof(float) : 0;
     return p;
 }
 
@@ -286,10 +285,10 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
         softmax_scale == -std::numeric_limits<float>::infinity())
         return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
     kivi::DecodePlan plan = kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len);
-    if (!d_ws || ws_bytes < plan.ws_bytes)
+    if (plan.ws_bytes > 0 && (!d_ws || ws_bytes < plan.ws_bytes))
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0,
                     plan.ws_bytes);
-    if (!aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     int err = kivi::launch_decode(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_slot_ids,
                                   d_seq_lens, d_block_table, bt_stride, softmax_scale, d_out,
                                   static_cast<float*>(d_ws), plan, stream);

@@ -41,12 +41,13 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 // Tiles per load buffer (two buffers per wave): deeper for the lighter
-// Value metadata of wide Value groups.
+// Value metadata of wide Value groups, and never more than the tiles of a
+// Key group (so at most one group begins inside a buffer).
 template <int NG>
-__host__ __device__ constexpr int buffer_tiles() { return NG == 1 ? 4 : (NG <= 4 ? 2 : 1); }
+__host__ __device__ constexpr int max_buffer_tiles() { return NG == 1 ? 4 : (NG <= 4 ? 2 : 1); }
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -59,8 +60,7 @@ struct DecodeArgs {
     int num_q_heads;
     int gqa;
     float scale_log2;
-    float* partials;
-    int* counters;    // one per (sequence, KV head); zero between calls
+    float* partials;  // [S][H_Q][n_splits] partials when n_splits > 1
     int n_splits;
     int tpg_shift;    // log2(tiles per Key group)
     int tpp_shift;    // log2(tiles per page)
@@ -261,11 +261,16 @@ __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
     return c;
 }
 
-// Physical page of tile t, or -1 when the table has none (tile skipped).
+// Block-table entry of tile t (unchecked; -1 past the table). Entries are
+// checked where they are used (valid_page), so the load is not waited on
+// here.
 __device__ __forceinline__ int page_of_tile(const DecodeArgs& a, const WgCtx& c, int t) {
     const int bi = t >> a.tpp_shift;
     if (t < 0 || bi >= c.bt_len) return -1;
-    const int blk = c.bt[bi];
+    return c.bt[bi];
+}
+// The page, or -1 when the entry names no block of the pool (tile skipped).
+__device__ __forceinline__ int valid_page(const DecodeArgs& a, int blk) {
     return (blk >= 0 && blk < a.v.num_blocks) ? blk : -1;
 }
 
@@ -494,9 +499,8 @@ struct TailRegs {
 // The 4 waves merge in LDS into one partial (m, l, o) per query head; the
 // last work group of a (sequence, KV head) to finish merges the partials:
 // m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
-template <int BITS, int DT, int NG>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
-    constexpr int kHalf = buffer_tiles<NG>();
+template <int BITS, int DT, int NG, int kHalf>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     constexpr int TILE_BYTES = kTile * kHeadDim * BITS / 8;
     constexpr int SLOT_BYTES = 4 * BITS;
     constexpr int NB = (BITS == 2) ? 2 : 1;  // Value pair-factor variants
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     // ---- tail tiles ----
     auto tail_issue = [&](int t, int tpage, TailRegs<BITS, NG>& x) {
         const int tb = (t >> a.tpg_shift) << a.tpg_shift;
-        x.blk = __builtin_amdgcn_readlane(tpage, t - tb);
+        x.blk = valid_page(a, __builtin_amdgcn_readlane(tpage, t - tb));
         const int blk = max(x.blk, 0);
         const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)c.h;
         const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
                 const uint2 u = buf_b64(rk, lane_code_off, coff);
                 x.kw[0] = u.x; x.kw[1] = u.y;
             }
-            const int mp = __builtin_amdgcn_ds_bpermute(4 * meta_tile, tpage);
+            const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * meta_tile, tpage));
             const uint32_t mo = k_meta_off(V, c.h, mp, nch);
             x.ms = buf_b128(rkm, mo, 0);
             x.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
@@ -670,8 +674,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     // range reads page 0 and is not computed), so a buffer is one straight
     // run of loads that the wait counts can follow. Each buffer also loads
     // the scales and zero-points of the Key group of its last tile: the only
-    // group that can begin inside a buffer when groups span >= kHalf tiles
-    // (other group starts load theirs when they are reached).
+    // group that can begin inside a buffer, as groups span >= kHalf tiles.
     struct Buf {
         TileRegs<BITS, NG> t[kHalf];
         bool ok[kHalf];
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < kHalf; ++e) {
             const int t = t0 + e;
-            const int blk = __builtin_amdgcn_readlane(my_page, (t - base) & 63);
+            const int blk = valid_page(a, __builtin_amdgcn_readlane(my_page, (t - base) & 63));
             b.ok[e] = blk >= 0 && t >= m_begin && t < m_end;
             const uint32_t chk = (uint32_t)(b.ok[e] ? blk : 0) * (uint32_t)H + (uint32_t)c.h;
             const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         // Key group of tile t0 + kHalf - 1 (its pages are in the window:
         // windows start on groups)
         const int gt = ((t0 + kHalf - 1) >> a.tpg_shift) << a.tpg_shift;
-        const int mp = __builtin_amdgcn_ds_bpermute(4 * ((gt + meta_tile - base) & 63), my_page);
+        const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * ((gt + meta_tile - base) & 63), my_page));
         const uint32_t mo = k_meta_off(V, c.h, mp, nch);
         b.ms = buf_b128(rkm, mo, 0);
         b.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
@@ -725,16 +728,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < kHalf; ++e) {
             const int t = t0 + e;
             if (!b.ok[e]) continue;
-            if ((t & (tpg - 1)) == 0 && t != m_begin) {
-                uint4 ms = b.ms, mz = b.mz;
-                if (e + tpg < kHalf) {  // short groups: this group's meta is not in the buffer
-                    const int mp = __builtin_amdgcn_ds_bpermute(4 * ((t + meta_tile - base) & 63), my_page);
-                    const uint32_t mo = k_meta_off(V, c.h, mp, nch);
-                    ms = buf_b128(rkm, mo, 0);
-                    mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
-                }
-                bias_l2 = build_table<BITS>(g, ms, mz, lq, lt, lbias, nr, sl2);
-            }
+            if ((t & (tpg - 1)) == 0 && t != m_begin)
+                bias_l2 = build_table<BITS>(g, b.ms, b.mz, lq, lt, lbias, nr, sl2);
             float sc[4], p[4];
             code_scores<BITS>(b.t[e].k, lt, lane_row, bias_l2, sl2, sc);
             st.update(sc, p);
@@ -766,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     uint4 ms0 = {0, 0, 0, 0}, mz0 = {0, 0, 0, 0};
     if (m_begin < m_end) {
         issue(t_first, ba);
-        const int mp = __builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page);
+        const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page));
         const uint32_t mo = k_meta_off(V, c.h, mp, nch);
         ms0 = buf_b128(rkm, mo, 0);
         mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
@@ -783,7 +778,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    // ---------------- merge the 4 waves in LDS ----------------
+    // ---------------- merge the waves in LDS ----------------
     {
         const float l_tot = xor_sum(st.l_acc);
         float zt[NG][NB];
@@ -828,56 +823,70 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
             lsum += f * sm_l[w * g + hn];
             osum += f * sm_o[(w * g + hn) * kHeadDim + chn];
         }
-        float* part = a.partials + (((size_t)c.s * HQ + c.h * g + hn) * a.n_splits + split) * kPartialStride;
-        if (chn == 0) {
-            part[0] = mstar;
-            part[1] = lsum;
-        }
-        part[4 + chn] = osum;
-    }
-
-    // ---------------- the last work group of this (sequence, KV head) merges ----------------
-    __shared__ int sm_last;
-    __syncthreads();  // every partial store of this work group precedes the release below
-    if (tid == 0) {
-        int* ctr = a.counters + (size_t)c.s * H + c.h;
-        const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = (prev == nvalid - 1);
-        if (sm_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every thread sees the other partials
-    for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
-        const int hn = idx / kHeadDim, chn = idx % kHeadDim;
-        const int hq = c.h * g + hn;
-        const float* pbase = a.partials + ((size_t)c.s * HQ + hq) * a.n_splits * kPartialStride;
-        float mstar = -INFINITY;
-        for (int i = 0; i < nvalid; ++i) mstar = fmaxf(mstar, pbase[(size_t)i * kPartialStride]);
-        float lsum = 0.0f, osum = 0.0f;
-        if (mstar != -INFINITY) {
-            for (int i = 0; i < nvalid; ++i) {
-                const float* pp = pbase + (size_t)i * kPartialStride;
-                const float mi = pp[0];
-                if (mi == -INFINITY) continue;
-                const float f = __builtin_amdgcn_exp2f(mi - mstar);
-                lsum += f * pp[1];
-                osum += f * pp[4 + chn];
+        if (nvalid == 1) {  // the only split: final output
+            a.out[((size_t)c.s * HQ + c.h * g + hn) * kHeadDim + chn] = from_f32<DT>(lsum > 0.0f ? osum / lsum : 0.0f);
+        } else {
+            float* part = a.partials + (((size_t)c.s * HQ + c.h * g + hn) * a.n_splits + split) * kPartialStride;
+            if (chn == 0) {
+                part[0] = mstar;
+                part[1] = lsum;
             }
+            part[4 + chn] = osum;
         }
-        const float o = lsum > 0.0f ? osum / lsum : 0.0f;
-        a.out[((size_t)c.s * HQ + hq) * kHeadDim + chn] = from_f32<DT>(o);
     }
 }
 
-template <int BITS, int DT>
-void launch_bits_dt(const DecodeArgs& a, int ng, dim3 grid, size_t lds, hipStream_t st) {
+// Merge of the split partials of one output element (sequence, query head,
+// channel) per thread, for sequences that used more than one split:
+// m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
+// A separate launch, so the partials of every split are visible.
+template <int DT>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int total) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int chn = idx % kHeadDim;
+    const int row = idx / kHeadDim;  // s * H_Q + hq
+    const int s = row / a.num_q_heads, hq = row % a.num_q_heads;
+    const WgCtx c = make_ctx(a, s, hq / a.gqa);
+    const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
+    if (nvalid == 1) return;  // written by its only split
+    const float* pbase = a.partials + (size_t)row * a.n_splits * kPartialStride;
+    float mstar = -INFINITY;
+    for (int i = 0; i < nvalid; ++i) mstar = fmaxf(mstar, pbase[(size_t)i * kPartialStride]);
+    float lsum = 0.0f, osum = 0.0f;
+    if (mstar != -INFINITY) {
+        for (int i = 0; i < nvalid; ++i) {
+            const float* pp = pbase + (size_t)i * kPartialStride;
+            const float mi = pp[0];
+            if (mi == -INFINITY) continue;
+            const float f = __builtin_amdgcn_exp2f(mi - mstar);
+            lsum += f * pp[1];
+            osum += f * pp[4 + chn];
+        }
+    }
+    a.out[(size_t)row * kHeadDim + chn] = from_f32<DT>(lsum > 0.0f ? osum / lsum : 0.0f);
+}
+
+template <int BITS, int DT, int NG>
+void launch_ng(const DecodeArgs& a, int tpg, dim3 grid, size_t lds, hipStream_t st) {
     dim3 block(kThreads);
+    constexpr int kMax = max_buffer_tiles<NG>();
+    const int kh = std::min(kMax, tpg);
+    if (kh >= 4 && kMax >= 4)
+        hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, (kMax >= 4 ? 4 : 1)>), grid, block, lds, st, a);
+    else if (kh >= 2 && kMax >= 2)
+        hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, (kMax >= 2 ? 2 : 1)>), grid, block, lds, st, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, 1>), grid, block, lds, st, a);
+}
+
+template <int BITS, int DT>
+void launch_bits_dt(const DecodeArgs& a, int ng, int tpg, dim3 grid, size_t lds, hipStream_t st) {
     switch (ng) {
-        case 1: hipLaunchKernelGGL((decode_kernel<BITS, DT, 1>), grid, block, lds, st, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BITS, DT, 2>), grid, block, lds, st, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BITS, DT, 4>), grid, block, lds, st, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<BITS, DT, 8>), grid, block, lds, st, a); break;
+        case 1: launch_ng<BITS, DT, 1>(a, tpg, grid, lds, st); break;
+        case 2: launch_ng<BITS, DT, 2>(a, tpg, grid, lds, st); break;
+        case 4: launch_ng<BITS, DT, 4>(a, tpg, grid, lds, st); break;
+        default: launch_ng<BITS, DT, 8>(a, tpg, grid, lds, st); break;
     }
 }
 
@@ -897,8 +906,7 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     a.num_q_heads = num_q_heads;
     a.gqa = num_q_heads / v.H;
     a.scale_log2 = softmax_scale * kLog2e;
-    a.counters = reinterpret_cast<int*>(partials);
-    a.partials = partials + plan.counter_floats;
+    a.partials = partials;
     a.n_splits = plan.n_splits;
     a.tpg_shift = __builtin_ctz((unsigned)(v.G / kTile));
     a.tpp_shift = __builtin_ctz((unsigned)(v.Bk / kTile));
@@ -910,12 +918,19 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     const int ng = kHeadDim / v.Gv;
     dim3 grid((unsigned)(num_seqs * v.H * plan.n_splits));
     const size_t lds = plan.lds_bytes;
+    const int tpg = v.G / kTile;
     if (v.bits == 4) {
-        if (v.dtype == kF16) launch_bits_dt<4, kF16>(a, ng, grid, lds, st);
-        else launch_bits_dt<4, kBF16>(a, ng, grid, lds, st);
+        if (v.dtype == kF16) launch_bits_dt<4, kF16>(a, ng, tpg, grid, lds, st);
+        else launch_bits_dt<4, kBF16>(a, ng, tpg, grid, lds, st);
     } else {
-        if (v.dtype == kF16) launch_bits_dt<2, kF16>(a, ng, grid, lds, st);
-        else launch_bits_dt<2, kBF16>(a, ng, grid, lds, st);
+        if (v.dtype == kF16) launch_bits_dt<2, kF16>(a, ng, tpg, grid, lds, st);
+        else launch_bits_dt<2, kBF16>(a, ng, tpg, grid, lds, st);
+    }
+    if (plan.n_splits > 1) {
+        const int total = num_seqs * num_q_heads * kHeadDim;
+        dim3 mgrid((unsigned)((total + 255) / 256));
+        if (v.dtype == kF16) hipLaunchKernelGGL((merge_kernel<kF16>), mgrid, dim3(256), 0, st, a, total);
+        else hipLaunchKernelGGL((merge_kernel<kBF16>), mgrid, dim3(256), 0, st, a, total);
     }
     return (int)hipGetLastError();
 }

@@ -34,13 +34,12 @@ CacheView view_of(const kivi_cache* c);
 
 // Split plan for decode: the grid has n_splits work groups per (sequence,
 // KV head); a sequence uses min(n_splits, ceil(main tiles / kMinSplitTiles))
-// of them (at least one). The workspace holds one merge counter per
-// (sequence, KV head), then the partials.
-constexpr int kMinSplitTiles = 32;
+// of them (at least one). With more than one split the workspace holds the
+// partials and a merge kernel follows.
+constexpr int kMinSplitTiles = 64;
 struct DecodePlan {
     int n_splits;
     size_t lds_bytes;   // dynamic LDS of one decode work group
-    size_t counter_floats;  // leading workspace words holding the merge counters
     size_t ws_bytes;
 };
 DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int max_seq_len);

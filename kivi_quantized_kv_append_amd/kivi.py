@@ -14,7 +14,8 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkivi.so")
+# KIVI_LIB may name another build of the same library (e.g. an instrumented one)
+LIB_PATH = os.environ.get("KIVI_LIB") or os.path.join(_HERE, "libkivi.so")
 
 KIVI_OK = 0
 KIVI_ERR_INVALID_ARG = 1

@@ -121,7 +121,8 @@ def test_call_argument_checks_launch_nothing():
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
         # decode: head ratio, workspace, pointers
         ws = kivi.kivi_decode_workspace_bytes(h, 4, 32, 4096)
-        assert ws > 0
+        assert ws > 0  # 32 (sequence, KV head) pairs: split, partials in the workspace
+        assert kivi.kivi_decode_workspace_bytes(h, 32, 32, 4096) == 0  # one work group per CU already
         with pytest.raises(kivi.KiviError) as e:
             kivi.kivi_decode_attention(h, 4, 30, D, D, D, 4096, D, 1, 0.1, D, D, ws)
         assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
