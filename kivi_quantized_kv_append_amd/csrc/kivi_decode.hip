@@ -316,22 +316,23 @@ __device__ __forceinline__ uint32_t k_meta_off(const CacheView& V, int h, int pa
 }
 
 // Query table of one Key group, built by one wave into its own LDS rows:
-//   hi/lo rows: Q'[n][c] = q[n][c] s[c] f(c) as an fp16 pair (hi + lo), where
-//   f(c) is the inverse place value of channel c's field in the code words;
-//   bias[n] = sum_c q[n][c] z[c] (fp16 products, fp32 sums).
+//   hi/lo rows: Q'[n][c] = sgn q[n][c] s[c] f(c) as an fp16 pair (hi + lo),
+//   where f(c) is the inverse place value of channel c's field in the code
+//   words and sgn the sign of the softmax scale;
+//   bias[n] = sgn sum_c q[n][c] z[c] (fp16 products, fp32 sums).
 // Lane (k = lane & 15, r = lane >> 4) covers channels 8k..8k+7 of heads
 // r, r+4, r+8, r+12. sv/zv: the lane's 8 scales and zero-points. Returns
-// bias[nr] * scale_log2 for this lane's score row nr.
+// bias[nr] for this lane's score row nr: the start of its score chains.
 template <int BITS>
 __device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const uint16_t* lq, uint8_t* lt, float* lbias,
-                                             int nr, float sl2) {
+                                             int nr, float sgn) {
     const int lane = threadIdx.x & 63, k = lane & 15, r = lane >> 4;
     const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
     const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
     h2 sf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float f = (BITS == 4) ? ((e & 1) ? 0.0625f : 1.0f) : 1.0f / (float)(1 << (2 * e));
+        const float f = sgn * ((BITS == 4) ? ((e & 1) ? 0.0625f : 1.0f) : 1.0f / (float)(1 << (2 * e)));
         sf[e] = __builtin_bit_cast(h2, sw[e]) * (h2){(_Float16)f, (_Float16)f};
     }
 #pragma unroll
@@ -356,26 +357,36 @@ __device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const ui
         if (ok) {
             *reinterpret_cast<uint4*>(lt + (2 * hn + 0) * kRowBytes + 16 * k) = (uint4){hw[0], hw[1], hw[2], hw[3]};
             *reinterpret_cast<uint4*>(lt + (2 * hn + 1) * kRowBytes + 16 * k) = (uint4){lw[0], lw[1], lw[2], lw[3]};
-            if (k == 0) lbias[hn] = zq;
+            if (k == 0) lbias[hn] = sgn * zq;
         }
     }
     // LDS operations of one wave complete in order; the fence keeps the
     // compiler from moving the reads below above the writes.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    return lbias[nr] * sl2;
+    return lbias[nr];
 }
 
-// Per-lane online-softmax state of query head (lane & 15) and its output
-// accumulators O^T[16 t + 4 (lane >> 4) + r][head] held in O[t][r].
-// wsum[gg][vb] sums the value-side weights (hi + lo) of channel group gg and
-// pair-factor variant vb: int4 codes carry a 1024 offset, so every output
-// channel holds 1024 * wsum too much until the merge takes it out.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+__device__ __forceinline__ float max4(f4 x) { return max2(max2(x[0], x[1]), max2(x[2], x[3])); }
+
+// Per-lane online-softmax state of query head (lane & 15). Scores are kept in
+// raw units (sgn q.k~); the weight of a score x is 2^((x - m) |scale| log2 e).
+// The running max m moves only when a score passes it by more than
+// kLazyLog2 / (|scale| log2 e): weights stay below 2^kLazyLog2 and the
+// rescale of the accumulators is rare.
+// O[t][r] holds O^T[16 t + 4 (lane >> 4) + r][head]; wsum[gg][vb] sums the
+// Value-side weights of channel group gg and pair-factor variant vb (int4
+// codes carry a 1024 offset, so each output channel holds 1024 wsum too
+// much until the merge takes it out).
+constexpr float kLazyLog2 = 2.0f;
+
 template <int NG, int NB>
 struct Acc {
-    float m_run, l_acc, zacc[NG], wsum[NG][NB];
+    float m_run, mneg, l_acc, zacc[NG], wsum[NG][NB];
     f4 O[8];
     __device__ __forceinline__ void init() {
         m_run = -INFINITY;
+        mneg = 0.0f;
         l_acc = 0.0f;
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg) {
@@ -386,14 +397,12 @@ struct Acc {
 #pragma unroll
         for (int t = 0; t < 8; ++t) O[t] = (f4){0.f, 0.f, 0.f, 0.f};
     }
-    // Scores of tokens 4j..4j+3 of one tile (exp2 domain) -> weights p.
-    // The rescale branch is taken by the whole wave when any head needs it
-    // (heads that do not get a factor of 1), so it never runs divergent.
-    __device__ __forceinline__ void update(const float sc[4], float p[4]) {
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mx = xor_max(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
-            const float f = mx > m_run ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+    // mx: this lane's largest new score (already reduced over the head's
+    // lanes). The branch is taken by the whole wave or not at all.
+    __device__ __forceinline__ void rescale(float mx, float sl2, float thr) {
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
+            const float mnew = max2(m_run, mx);
+            const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - mnew) * sl2);
             l_acc *= f;
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
@@ -403,70 +412,95 @@ struct Acc {
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) O[t] *= f;
-            m_run = fmaxf(m_run, mx);
+            m_run = mnew;
+            mneg = -mnew * sl2;
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
-        l_acc += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    __device__ __forceinline__ float weight(float x, float sl2) const {
+        return __builtin_amdgcn_exp2f(__builtin_fmaf(x, sl2, mneg));
     }
 };
 
-// Scores (exp2 domain) of a 16-token tile whose Keys are quantised: the
-// group's B-operands come straight from the wave's LDS table; two
-// accumulation chains (hi, lo). `row`: the lane's byte offset into the table
-// (head row nr, k-slice 16 j).
+// Raw scores of a 16-token tile whose Keys are quantised: one accumulation
+// chain that starts at the zero-point bias and takes the group's hi and lo
+// B-operands from the wave's LDS table. `row`: the lane's byte offset into
+// the table (head row nr, k-slice 16 j).
 template <int BITS>
-__device__ __forceinline__ void code_scores(const uint32_t* kw, const uint8_t* lt, int row, float bias_l2, float sl2,
-                                            float sc[4]) {
+__device__ __forceinline__ f4 code_scores(const uint32_t* kw, const uint8_t* lt, int row, float bias) {
     h8 A[4];
     unpack_k<BITS>(kw, A);
-    f4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+    f4 acc = {bias, bias, bias, bias};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const h8 bh = *reinterpret_cast<const h8*>(lt + row + 64 * i);
         const h8 bl = *reinterpret_cast<const h8*>(lt + row + kRowBytes + 64 * i);
-        ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bh, ah, 0, 0, 0);
-        al = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bl, al, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bl, acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (ah[r] + al[r]) * sl2 + bias_l2;
+    return acc;
 }
 
-// Value side of a main tile: W = p * scale (hi, lo) per channel group and
-// pair-factor variant, zero-points through zacc, one MFMA per channel tile.
+// fp16 pair of the low (scale) or high (zero-point) halves of two meta words.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+
+// Value side of two main tiles (A, B): one MFMA per 16-channel tile covers
+// both, with k = (tile A tokens 4j..4j+3, tile B tokens 4j..4j+3) in each
+// lane; its A-operand holds the codes, its B-operand the fp16 weights
+// p * scale / F (F: the place value of the token's code field). Zero-points
+// go through zacc. With `only_a` tile B's weights are zero.
 template <int BITS, int NG, int NB>
-__device__ __forceinline__ void value_tile(Acc<NG, NB>& st, const uint32_t* vw, const uint32_t* vm, const float p[4]) {
-    h8 Bv[NG][NB];
+__device__ __forceinline__ void value_pair(Acc<NG, NB>& st, const uint32_t* vwa, const uint32_t* vma,
+                                           const uint32_t* vwb, const uint32_t* vmb, const float pa[4],
+                                           const float pb[4]) {
+    constexpr float kF23 = (BITS == 4) ? 0.0625f : 0.25f;  // 1/F of tokens r = 2, 3
+    const h2 qa01 = {(_Float16)pa[0], (_Float16)pa[1]};
+    const h2 qa23 = {(_Float16)(pa[2] * kF23), (_Float16)(pa[3] * kF23)};
+    const h2 qb01 = {(_Float16)pb[0], (_Float16)pb[1]};
+    const h2 qb23 = {(_Float16)(pb[2] * kF23), (_Float16)(pb[3] * kF23)};
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    uint32_t Bw[NG][NB][4];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-        float Sv[4];
+        const h2 wa01 = qa01 * __builtin_bit_cast(h2, lo_halves(vma[0 * NG + gg], vma[1 * NG + gg]));
+        const h2 wa23 = qa23 * __builtin_bit_cast(h2, lo_halves(vma[2 * NG + gg], vma[3 * NG + gg]));
+        const h2 wb01 = qb01 * __builtin_bit_cast(h2, lo_halves(vmb[0 * NG + gg], vmb[1 * NG + gg]));
+        const h2 wb23 = qb23 * __builtin_bit_cast(h2, lo_halves(vmb[2 * NG + gg], vmb[3 * NG + gg]));
+        Bw[gg][0][0] = __builtin_bit_cast(uint32_t, wa01);
+        Bw[gg][0][1] = __builtin_bit_cast(uint32_t, wa23);
+        Bw[gg][0][2] = __builtin_bit_cast(uint32_t, wb01);
+        Bw[gg][0][3] = __builtin_bit_cast(uint32_t, wb23);
+        if constexpr (BITS == 4) {
+            // the exact fp16 weights the MFMA multiplies the 1024 offsets with
+            float ws = __builtin_amdgcn_fdot2(wa01, one, st.wsum[gg][0], false);
+            ws = __builtin_amdgcn_fdot2(wa23, one, ws, false);
+            ws = __builtin_amdgcn_fdot2(wb01, one, ws, false);
+            st.wsum[gg][0] = __builtin_amdgcn_fdot2(wb23, one, ws, false);
+        } else {
+            // odd channel tiles: fields 4 places up (factor 1/16)
+            const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+            Bw[gg][1][0] = __builtin_bit_cast(uint32_t, wa01 * k16);
+            Bw[gg][1][1] = __builtin_bit_cast(uint32_t, wa23 * k16);
+            Bw[gg][1][2] = __builtin_bit_cast(uint32_t, wb01 * k16);
+            Bw[gg][1][3] = __builtin_bit_cast(uint32_t, wb23 * k16);
+        }
+        float z = st.zacc[gg];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t mw = vm[r * NG + gg];
-            Sv[r] = f16_bits_to_f32((uint16_t)(mw & 0xFFFFu));
-            st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
+            z += pa[r] * f16_bits_to_f32((uint16_t)(vma[r * NG + gg] >> 16));
+            z += pb[r] * f16_bits_to_f32((uint16_t)(vmb[r * NG + gg] >> 16));
         }
-#pragma unroll
-        for (int vb = 0; vb < NB; ++vb) {
-            float ws = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float wv = p[r] * Sv[r] * v_inv_factor<BITS>(vb, r);
-                _Float16 hi, lo;
-                split_f16(wv, hi, lo);
-                Bv[gg][vb][r] = hi;
-                Bv[gg][vb][4 + r] = lo;
-                ws += wv;
-            }
-            st.wsum[gg][vb] += ws;
-        }
+        st.zacc[gg] = z;
     }
-    h4 Av[8];
-    unpack_v<BITS>(vw, Av);
+    h4 Aa[8], Ab[8];
+    unpack_v<BITS>(vwa, Aa);
+    unpack_v<BITS>(vwb, Ab);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
         const int gg = (16 * tt) / (kHeadDim / NG);
-        st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(Av[tt]), Bv[gg][tt % NB], st.O[tt], 0, 0, 0);
+        const uint32_t* bw = Bw[gg][tt % NB];
+        const h8 Bv = make_h8(bw[0], bw[1], bw[2], bw[3]);
+        const h8 Av = (h8){Aa[tt][0], Aa[tt][1], Aa[tt][2], Aa[tt][3], Ab[tt][0], Ab[tt][1], Ab[tt][2], Ab[tt][3]};
+        st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Bv, st.O[tt], 0, 0, 0);
     }
 }
 
@@ -523,7 +557,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int tpg = 1 << a.tpg_shift, tpp = 1 << a.tpp_shift;
     const int nch = kHeadDim * V.Bk / V.G;  // Key channels whose meta one page holds
     const int meta_tile = (8 * (lane & 15) / nch) * tpp;  // tile (in its group) whose page holds this lane's meta
-    const float sl2 = a.scale_log2;
+    // weights 2^(x |scale| log2 e) of raw scores x = sgn q.k (sgn folded into the tables)
+    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;
+    const float sl2 = fabsf(a.scale_log2);
+    const float thr = sl2 > 0.0f ? kLazyLog2 / sl2 : 0.0f;  // lazy-max threshold in raw units
     const int HQ = a.num_q_heads;
 
     const int nslots = kWaves * nvalid;
@@ -619,10 +656,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     auto tail_compute = [&](int t, const TailRegs<BITS, NG>& x) {
         if (x.blk < 0) return;
         const int p0 = t * kTile, pq = p0 + 4 * j;
-        float sc[4];
+        f4 raw;
         if (t < tk_tiles) {
-            const float bias_l2 = build_table<BITS>(g, x.ms, x.mz, lq, lt, lbias, nr, sl2);
-            code_scores<BITS>(x.kw, lt, lane_row, bias_l2, sl2, sc);
+            const float bias = build_table<BITS>(g, x.ms, x.mz, lq, lt, lbias, nr, sgn);
+            raw = code_scores<BITS>(x.kw, lt, lane_row, bias);
         } else {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             const uint8_t* qrow = reinterpret_cast<const uint8_t*>(lq + nr * kQRow);
@@ -635,11 +672,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 const h8 B = *reinterpret_cast<const h8*>(qrow + 2 * (32 * i + 8 * j));
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[r] = (p0 + 4 * j + r < T) ? acc[r] * sl2 : -INFINITY;
+            raw = acc * sgn;
         }
-        float p[4];
-        st.update(sc, p);
+        // tokens at or past T take no part (weight 0, not in the max)
+        float p[4], mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (pq + r < T) mx = max2(mx, raw[r]);
+        st.rescale(xor_max(mx), sl2, thr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = (pq + r < T) ? st.weight(raw[r], sl2) : 0.0f;
+        st.l_acc += (p[0] + p[1]) + (p[2] + p[3]);
         // Value token r: code (< TV), residual (< T) or masked, chosen by
         // selects (no divergent branches)
 #pragma unroll
@@ -722,18 +765,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         b.ms = buf_b128(rkm, mo, 0);
         b.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
     };
-    float bias_l2 = 0.0f;
+    float bias = 0.0f;
+    // Tiles are taken in pairs (slots e, e + 1 of a buffer; both in one Key
+    // group, as pairs start an even number of tiles after a group start).
     auto compute = [&](const Buf& b, int t0) {
 #pragma unroll
-        for (int e = 0; e < kHalf; ++e) {
+        for (int e = 0; e < kHalf; e += 2) {
             const int t = t0 + e;
-            if (!b.ok[e]) continue;
-            if ((t & (tpg - 1)) == 0 && t != m_begin)
-                bias_l2 = build_table<BITS>(g, b.ms, b.mz, lq, lt, lbias, nr, sl2);
-            float sc[4], p[4];
-            code_scores<BITS>(b.t[e].k, lt, lane_row, bias_l2, sl2, sc);
-            st.update(sc, p);
-            value_tile<BITS, NG, NB>(st, b.t[e].v, b.t[e].vm, p);
+            constexpr bool kPair = kHalf > 1;
+            const bool oka = b.ok[e], okb = kPair ? b.ok[kPair ? e + 1 : e] : false;
+            if (!oka && !okb) continue;
+            if ((t & (tpg - 1)) == 0 && t != m_begin) bias = build_table<BITS>(g, b.ms, b.mz, lq, lt, lbias, nr, sgn);
+            const TileRegs<BITS, NG>& ta = b.t[e];
+            const TileRegs<BITS, NG>& tb = b.t[kPair ? e + 1 : e];
+            const f4 ra = code_scores<BITS>(ta.k, lt, lane_row, bias);
+            f4 rb = ra;
+            if (kPair) rb = code_scores<BITS>(tb.k, lt, lane_row, bias);
+            float mx = oka ? max4(ra) : -INFINITY;
+            if (okb) mx = max2(mx, max4(rb));
+            st.rescale(xor_max(mx), sl2, thr);
+            float pa[4], pb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pa[r] = oka ? st.weight(ra[r], sl2) : 0.0f;
+                pb[r] = okb ? st.weight(rb[r], sl2) : 0.0f;
+            }
+            st.l_acc += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
+            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb);
         }
     };
 
@@ -768,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
     if constexpr (NG < 4) run_tail();
     if (m_begin < m_end) {
-        bias_l2 = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sl2);
+        bias = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
         for (int t0 = t_first; t0 < m_end; t0 += 2 * kHalf) {
             issue(t0 + kHalf, bb);
             compute(ba, t0);
@@ -793,8 +851,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         float* sm_l = sm_m + kWaves * g;               // [kWaves][g]
         float* sm_o = sm_l + kWaves * g;               // [kWaves][g][128]
         if (n < g) {
-            if (j == 0) {
-                sm_m[wave * g + n] = st.m_run;
+            if (j == 0) {  // the running max in log2 units
+                sm_m[wave * g + n] = st.m_run == -INFINITY ? -INFINITY : st.m_run * sl2;
                 sm_l[wave * g + n] = l_tot;
             }
 #pragma unroll
