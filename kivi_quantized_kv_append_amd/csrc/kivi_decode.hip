@@ -546,8 +546,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const WgCtx c = make_ctx(a, sh / H, sh % H);
     // at least kMinSplitTiles main tiles per split when there are that many
     const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
-    if (split >= nvalid) return;
     const int tid = threadIdx.x, lane = tid & 63;
+    if (split >= nvalid) {  // no work: an empty partial for the merge
+        if (tid < c.g)
+            a.partials[(((size_t)c.s * a.num_q_heads + c.h * c.g + tid) * a.n_splits + split) * kPartialStride] =
+                -INFINITY;
+        return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, j = lane >> 4;
     const int g = c.g;
@@ -881,7 +886,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             lsum += f * sm_l[w * g + hn];
             osum += f * sm_o[(w * g + hn) * kHeadDim + chn];
         }
-        if (nvalid == 1) {  // the only split: final output
+        if (a.n_splits == 1) {  // no split anywhere: final output
             a.out[((size_t)c.s * HQ + c.h * g + hn) * kHeadDim + chn] = from_f32<DT>(lsum > 0.0f ? osum / lsum : 0.0f);
         } else {
             float* part = a.partials + (((size_t)c.s * HQ + c.h * g + hn) * a.n_splits + split) * kPartialStride;
@@ -894,35 +899,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// Merge of the split partials of one output element (sequence, query head,
-// channel) per thread, for sequences that used more than one split:
+// Merge of the split partials of one (sequence, query head): one work group
+// of 128 threads (one per channel), one pass with a running maximum:
 // m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
-// A separate launch, so the partials of every split are visible.
+// Splits without work left m_i = -inf. A separate launch, so the partials of
+// every split are visible.
 template <int DT>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int total) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const int chn = idx % kHeadDim;
-    const int row = idx / kHeadDim;  // s * H_Q + hq
-    const int s = row / a.num_q_heads, hq = row % a.num_q_heads;
-    const WgCtx c = make_ctx(a, s, hq / a.gqa);
-    const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
-    if (nvalid == 1) return;  // written by its only split
-    const float* pbase = a.partials + (size_t)row * a.n_splits * kPartialStride;
-    float mstar = -INFINITY;
-    for (int i = 0; i < nvalid; ++i) mstar = fmaxf(mstar, pbase[(size_t)i * kPartialStride]);
-    float lsum = 0.0f, osum = 0.0f;
-    if (mstar != -INFINITY) {
-        for (int i = 0; i < nvalid; ++i) {
-            const float* pp = pbase + (size_t)i * kPartialStride;
-            const float mi = pp[0];
-            if (mi == -INFINITY) continue;
-            const float f = __builtin_amdgcn_exp2f(mi - mstar);
-            lsum += f * pp[1];
-            osum += f * pp[4 + chn];
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(DecodeArgs a) {
+    constexpr int kBatch = 8;
+    const int row = blockIdx.x;  // s * H_Q + hq
+    const int chn = threadIdx.x;
+    const int ns = a.n_splits;
+    const float* pbase = a.partials + (size_t)row * ns * kPartialStride;
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    for (int i0 = 0; i0 < ns; i0 += kBatch) {
+        float mi[kBatch], li[kBatch], oi[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {  // independent loads, issued together
+            const float* pp = pbase + (size_t)min(i0 + k, ns - 1) * kPartialStride;
+            mi[k] = i0 + k < ns ? pp[0] : -INFINITY;
+            li[k] = pp[1];
+            oi[k] = pp[4 + chn];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (mi[k] == -INFINITY) continue;
+            const float mn = fmaxf(m, mi[k]);
+            const float fo = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+            const float fi = __builtin_amdgcn_exp2f(mi[k] - mn);
+            l = l * fo + li[k] * fi;
+            o = o * fo + oi[k] * fi;
+            m = mn;
         }
     }
-    a.out[(size_t)row * kHeadDim + chn] = from_f32<DT>(lsum > 0.0f ? osum / lsum : 0.0f);
+    a.out[(size_t)row * kHeadDim + chn] = from_f32<DT>(l > 0.0f ? o / l : 0.0f);
 }
 
 template <int BITS, int DT, int NG>
@@ -985,10 +995,9 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
         else launch_bits_dt<2, kBF16>(a, ng, tpg, grid, lds, st);
     }
     if (plan.n_splits > 1) {
-        const int total = num_seqs * num_q_heads * kHeadDim;
-        dim3 mgrid((unsigned)((total + 255) / 256));
-        if (v.dtype == kF16) hipLaunchKernelGGL((merge_kernel<kF16>), mgrid, dim3(256), 0, st, a, total);
-        else hipLaunchKernelGGL((merge_kernel<kBF16>), mgrid, dim3(256), 0, st, a, total);
+        dim3 mgrid((unsigned)(num_seqs * num_q_heads));
+        if (v.dtype == kF16) hipLaunchKernelGGL((merge_kernel<kF16>), mgrid, dim3(kHeadDim), 0, st, a);
+        else hipLaunchKernelGGL((merge_kernel<kBF16>), mgrid, dim3(kHeadDim), 0, st, a);
     }
     return (int)hipGetLastError();
 }
