@@ -12,6 +12,11 @@
 // Phase A (all quantisation) reads the old ring and the new rows; a barrier
 // separates it from phase B (ring writes), which may overwrite ring slots
 // phase A read. Distinct sequences touch disjoint pages and ring slots.
+//
+// Bulk appends (a prefill chunk) split phase A over gridDim.y parts per
+// (sequence, head): Key groups and Value token quads are dealt round-robin,
+// every unit writes disjoint code words and metadata, and phase B then runs
+// as a second launch on the same stream, after every part has read the ring.
 
 #include "kivi_device.h"
 #include "kivi_internal.h"
@@ -31,6 +36,7 @@ struct AppendArgs {
     const uint16_t* v_new;
     const int32_t* block_table;
     int bt_stride;
+    int mode;  // 0: phases A and B; 1: phase A only (split over gridDim.y); 2: phase B only
 };
 
 template <int BITS, int DT>
@@ -43,6 +49,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     const int s = blockIdx.x / H;
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x;
+    const int part = blockIdx.y, nparts = gridDim.y;
 
     const int slot = a.slot_ids[s];
     const int T0 = a.seq_lens_before[s];
@@ -83,12 +90,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     __shared__ float sm_v[4][4][kHeadDim];
     __shared__ float sm_vp[4][4][8][2];
 
+    if (a.mode != 2) {
     // ---------------- phase A1: Key flush, one group at a time ----------------
     {
         const int c = tid & (kHeadDim - 1);
         const int half = tid >> 7;
         const int nch = kHeadDim * Bk / G;  // channels per K-meta page slot
-        for (int j = TK0 / G; j < TK1 / G; ++j) {
+        for (int j = TK0 / G + part; j < TK1 / G; j += nparts) {
             const int base = j * G;
             const int lo = half * (G / 2), hi = lo + G / 2;
             float mn = INFINITY, mx = -INFINITY;
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const int gw = Gv / 2;  // lanes per channel group (two channels per lane)
         const int q_lo = TV0 / 4, q_hi = (TV1 + 3) / 4;
         const int rounds = TV1 > TV0 ? (q_hi - q_lo + 3) / 4 : 0;
-        for (int rd = 0; rd < rounds; ++rd) {
+        for (int rd = part; rd < rounds; rd += nparts) {
             const int qd = q_lo + rd * 4 + wave;
             const bool active = qd < q_hi;
             const int p0 = 4 * qd;
@@ -243,6 +251,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         }
     }
 
+    }  // phase A
+    if (a.mode == 1) return;
     __syncthreads();
 
     // ---------------- phase B: new rows that stay in the residual ----------------
@@ -269,7 +279,6 @@ int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
                   const int32_t* seq_lens_before, const int32_t* cu_new, int max_new,
                   const void* k_new, const void* v_new, const int32_t* block_table, int bt_stride,
                   void* stream) {
-    (void)max_new;
     AppendArgs a;
     a.v = v;
     a.slot_ids = slot_ids;
@@ -279,14 +288,25 @@ int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
     a.v_new = static_cast<const uint16_t*>(v_new);
     a.block_table = block_table;
     a.bt_stride = bt_stride;
-    dim3 grid((unsigned)(num_seqs * v.H)), block(kAppendThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (v.bits == 4) {
-        if (v.dtype == kF16) hipLaunchKernelGGL((append_kernel<4, kF16>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((append_kernel<4, kBF16>), grid, block, 0, st, a);
+    auto launch = [&](int mode, int parts) {
+        a.mode = mode;
+        dim3 grid((unsigned)(num_seqs * v.H), (unsigned)parts), block(kAppendThreads);
+        if (v.bits == 4) {
+            if (v.dtype == kF16) hipLaunchKernelGGL((append_kernel<4, kF16>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((append_kernel<4, kBF16>), grid, block, 0, st, a);
+        } else {
+            if (v.dtype == kF16) hipLaunchKernelGGL((append_kernel<2, kF16>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((append_kernel<2, kBF16>), grid, block, 0, st, a);
+        }
+    };
+    // max_new only sizes the split; every part count covers every unit
+    const int parts = append_parts(max_new);
+    if (parts <= 1) {
+        launch(0, 1);
     } else {
-        if (v.dtype == kF16) hipLaunchKernelGGL((append_kernel<2, kF16>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((append_kernel<2, kBF16>), grid, block, 0, st, a);
+        launch(1, parts);
+        launch(2, 1);
     }
     return (int)hipGetLastError();
 }

@@ -47,6 +47,14 @@ size_t decode_lds_bytes(int gqa);
 
 constexpr int kPartialStride = 132;  // floats per partial: m, l, pad, pad, o[128]
 
+// Work groups per (sequence, KV head) for the quantisation phase of an
+// append of up to max_new rows per sequence: one part per 64 new rows, at
+// most 64 parts. One part runs the whole append in a single launch.
+inline int append_parts(int max_new) {
+    const int p = (max_new + 63) / 64;
+    return p < 1 ? 1 : (p > 64 ? 64 : p);
+}
+
 // Kernel launchers (return a hipError_t as int).
 int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
                   const int32_t* seq_lens_before, const int32_t* cu_new, int max_new,

@@ -66,6 +66,16 @@ def test_append_variants_bitexact(bits, G, Gv, R, Bk, H, dtype):
 
 
 @pytest.mark.parametrize("bits", [4, 2])
+def test_bulk_append_split_over_many_parts(bits):
+    """Large single-call appends (a prefill chunk): the quantisation is split
+    over up to 64 work groups per (sequence, head), after a partly filled
+    residual and a partly filled Value quad."""
+    w = _variant(1, bits=bits, k_group=64, v_group=32, residual=128, num_kv_heads=2, num_q_heads=8,
+                 num_seqs=3, seq_lens=[4100, 2222, 77], shuffle=True, pool_factor=1.3, n_outlier=2)
+    _append_and_compare(w, [3, 130, 4096], decode_every=True)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
 def test_decode_ragged_batch_llama_shape(bits):
     """Reduced Llama-3-8B shape (32 Q / 8 KV heads): ragged lengths around the
     residual and tile edges, one bulk append then decode."""
