@@ -15,6 +15,12 @@ Prints one JSON line. `value` is algorithmic HBM GB/s of the attention
 (codes + group metadata once + residual + q/out + page table) per whole step;
 `roofline` relates the same bytes to the decode call's own duration, timed
 with HIP events on the stream it was launched on.
+
+The `prefill` object times chunked prefill on the Qwen2.5-7B head shape
+(8 requests x 16384 cached tokens + a 512-token causal chunk, 28 Q / 4 KV
+heads, bf16, int4 G=R=128): the chunk's bulk append once, then prefill
+attention launches back to back, reported as useful TFLOP/s against the
+dense bf16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -32,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 matrix-core peak
 MALL_BYTES = 256 << 20
 
 
@@ -44,6 +51,8 @@ def parse():
     ap.add_argument("--bits", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="0 = size for ~10-30 s")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the timed steps "
                          "(a known-size kernel for scaling hardware byte counters)")
@@ -65,6 +74,105 @@ def decode_bytes(lens, w) -> int:
                     + (T - TK) * d * es + (T - TV) * d * es + 2 * g * d * es)
         total += per_head * w.num_kv_heads + 4 * math.ceil(T / w.block_size)
     return total
+
+
+def prefill_flop(cached: int, chunk: int, num_q_heads: int, num_seqs: int, d: int = 128) -> int:
+    """Useful FLOP of causal chunked prefill: query i of a chunk sees cached + i + 1
+    tokens; QK^T and PV each take 2 d FLOP per (query, head, visible token)."""
+    visible = chunk * cached + chunk * (chunk + 1) // 2
+    return 4 * d * visible * num_q_heads * num_seqs
+
+
+def prefill_leg(torch, kivi, inputs, dev, n_iter: int, check: bool):
+    """Chunked prefill on the Qwen2.5-7B head shape (8 requests, 16384 cached tokens,
+    512-token causal chunk, bf16, int4 G=R=128): bulk-append the chunk, then time
+    prefill attention launches back to back with HIP events on their stream."""
+    w = inputs.config(5)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    P, C = int(w.seq_lens[0]), int(w.extra_tokens)
+    streams = [w.kv_stream(s) for s in range(S)]
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, w.num_blocks, S, w.dtype)
+    nbytes = kivi.kivi_cache_pool_bytes(cfg)
+    pool = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    h = kivi.kivi_cache_create(cfg, pool, nbytes)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    lens_p = torch.full((S,), P, dtype=torch.int32, device=dev)
+    lens_t = torch.full((S,), P + C, dtype=torch.int32, device=dev)
+    cu_p = torch.arange(0, (S + 1) * P, P, dtype=torch.int32, device=dev)
+    cu_c = torch.arange(0, (S + 1) * C, C, dtype=torch.int32, device=dev)
+    kp = dev_u16(np.concatenate([streams[s][0][:P] for s in range(S)]))
+    vp = dev_u16(np.concatenate([streams[s][1][:P] for s in range(S)]))
+    kc = dev_u16(np.concatenate([streams[s][0][P:] for s in range(S)]))
+    vc = dev_u16(np.concatenate([streams[s][1][P:] for s in range(S)]))
+    q_bits = inputs.to_bits(np.random.default_rng(7).standard_normal((S * C, HQ, d)), w.dtype)
+    q = dev_u16(q_bits)
+    out = torch.empty((S * C, HQ, d), dtype=torch.int16, device=dev)
+    ws_bytes = kivi.kivi_prefill_workspace_bytes(h, S, HQ, C, P + C)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        kivi.kivi_append_tokens(h, S, slots, zeros, cu_p, P, kp, vp, bt, bt.shape[1], stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kivi.kivi_append_tokens(h, S, slots, lens_p, cu_c, C, kc, vc, bt, bt.shape[1], stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        append_us = e0.elapsed_time(e1) * 1e3
+
+        def run():
+            kivi.kivi_prefill_attention(h, S, HQ, q, cu_c, C, slots, lens_t, P + C, bt, bt.shape[1], scale, 1,
+                                        out, ws, ws_bytes, stream)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_iter + 1)]
+        ev[0].record(stream)
+        for i in range(n_iter):
+            run()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n_iter)])
+    flop = prefill_flop(P, C, HQ, S, d)
+    tflops = flop / (float(ms.mean()) * 1e-3) / 1e12
+    res = {"workload": w.name, "num_seqs": S, "cached": P, "chunk": C, "q_heads": HQ, "kv_heads": H,
+           "dtype": "bf16", "bits": w.bits, "k_group": w.k_group, "residual": w.residual,
+           "chunk_append_us": round(append_us, 1),
+           "prefill_us_mean": round(float(ms.mean()) * 1e3, 1),
+           "prefill_us_min": round(float(ms.min()) * 1e3, 1),
+           "flop_per_launch": flop,
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "kernel": "prefill_kernel, one kivi_prefill_attention call"}}
+    if check:
+        import oracle
+        got = out.cpu().numpy().view(np.uint16)
+        caches = []
+        for s in range(S):
+            c = oracle.SeqCache(H, d, w.bits, w.k_group, w.v_group, w.residual, w.dtype, P + C)
+            c.append(streams[s][0], streams[s][1])
+            caches.append(c)
+        rng = np.random.default_rng(11)
+        rows = np.concatenate([np.arange(0, S * C, C), np.arange(C - 1, S * C, C),
+                               rng.integers(0, S * C, 48)]).astype(np.int32)
+        heads = rng.integers(0, HQ, rows.size).astype(np.int32)
+        cu = np.arange(0, (S + 1) * C, C)
+        ref = oracle.attention(caches, HQ, q_bits, w.dtype, cu, scale, True, rows, heads,
+                               threads=oracle.hardware_threads())
+        g32 = inputs.bits_to_float(got[rows, heads], w.dtype).astype(np.float64)
+        r32 = ref.astype(np.float32).astype(np.float64)
+        err = np.abs(g32 - r32)
+        res["parity"] = {"sampled_rows": int(rows.size), "max_abs": float(err.max()),
+                         "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
+    kivi.kivi_cache_destroy(h)
+    return res
 
 
 def kernel_source_hash() -> str:
@@ -314,6 +422,9 @@ def main():
     }
     for h in handles:
         kivi.kivi_cache_destroy(h)
+    del pools, step_k, step_v, step_q
+    if not args.no_prefill:
+        res["prefill"] = prefill_leg(torch, kivi, inputs, dev, args.prefill_iters, not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 

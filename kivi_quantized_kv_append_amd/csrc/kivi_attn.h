@@ -290,7 +290,35 @@ struct Acc {
     __device__ __forceinline__ float weight(float x, float sl2) const {
         return __builtin_amdgcn_exp2f(__builtin_fmaf(x, sl2, mneg));
     }
+    // Take the int4 1024 offsets accumulated so far out of O. An accumulator
+    // that carries them is ~137 times larger than its useful part (code
+    // fields of 0..15 under 1024), so fp32 rounding in the MFMA sums grows
+    // with the tokens summed; flushing every few hundred tokens bounds it.
+    // Wave-uniform call.
+    template <int BITS>
+    __device__ __forceinline__ void flush_offsets() {
+        if constexpr (BITS == 4) {
+            float c[NG][NB];
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+                for (int vb = 0; vb < NB; ++vb) {
+                    c[gg][vb] = -1024.0f * xor_sum(wsum[gg][vb]);
+                    wsum[gg][vb] = 0.0f;
+                }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                const float x = c[(16 * tt) / (kHeadDim / NG)][tt % NB];
+                O[tt] += (f4){x, x, x, x};
+            }
+        }
+    }
 };
+
+// Main-loop iterations (each 2 kHalf tiles) between two offset flushes: about
+// 16 tile pairs.
+template <int kHalf>
+constexpr int flush_period() { return 16 / kHalf > 0 ? 16 / kHalf : 1; }
 
 // Raw scores of a 16-token tile whose Keys are quantised: one accumulation
 // chain that starts at the zero-point bias and takes the group's hi and lo

@@ -458,12 +458,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     if constexpr (NG < 4) run_tail();
     if (m_begin < m_end) {
         bias = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
+        int it = 0;
         for (int t0 = t_first; t0 < m_end; t0 += 2 * kHalf) {
             issue(t0 + kHalf, bb);
             compute(ba, t0);
             if (t0 + kHalf >= m_end) break;
             issue(t0 + 2 * kHalf, ba);
             compute(bb, t0 + kHalf);
+            if (++it == flush_period<kHalf>()) {
+                it = 0;
+                st.template flush_offsets<BITS>();
+            }
         }
     }
 

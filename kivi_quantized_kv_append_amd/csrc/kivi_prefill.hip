@@ -258,12 +258,17 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         const uint4 ms0 = buf_b128(rkm, mo, 0);
         const uint4 mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
         bias = build_table<BITS>(kRowsPerWave, ms0, mz0, lq, lt, lbias, n, sgn);
+        int it = 0;
         for (int t0 = 0; t0 < m_end; t0 += 2 * kHalf) {
             issue(t0 + kHalf, bb);
             compute(ba, t0);
             if (t0 + kHalf >= m_end) break;
             issue(t0 + 2 * kHalf, ba);
             compute(bb, t0 + kHalf);
+            if (++it == flush_period<kHalf>()) {
+                it = 0;
+                st.template flush_offsets<BITS>();
+            }
         }
     }
 

@@ -54,3 +54,27 @@ def test_prefill_gqa_extremes(g):
     w = inputs.config(2, num_seqs=2, num_kv_heads=2, num_q_heads=2 * g, seq_lens=[500, 260],
                       extra_tokens=40, shuffle=True, pool_factor=1.25)
     _prefill_case(w, [40, 25], causal=True)
+
+
+def test_prefill_qwen_full_size_sampled():
+    """Full Qwen2.5-7B prefill workload (8 requests x 16384 cached + a 512-token
+    chunk, bf16, int4 G=R=128), in the launch configuration the benchmark times:
+    the chunk is bulk-appended in one call, every output is computed, and a
+    sample of (row, head) outputs is checked against the oracle, including the
+    first and last row of every request."""
+    w = inputs.config(5)
+    S, C, P = w.num_seqs, w.extra_tokens, int(w.seq_lens[0])
+    gc = GpuCache(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(S)])
+    gc.append([r[:P] for r in rk], [r[:P] for r in rv])
+    gc.append([r[P:] for r in rk], [r[P:] for r in rv])
+    orc = oracle_caches(w, lens=w.final_lens)
+    cu = np.arange(0, (S + 1) * C, C)
+    q = inputs.to_bits(np.random.default_rng(7).standard_normal((S * C, w.num_q_heads, 128)), w.dtype)
+    got = gc.prefill(q, cu, SCALE, causal=True)
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([np.arange(0, S * C, C), np.arange(C - 1, S * C, C),
+                           rng.integers(0, S * C, 200)]).astype(np.int32)
+    heads = rng.integers(0, w.num_q_heads, rows.size).astype(np.int32)
+    ref = oracle.attention(orc, w.num_q_heads, q, w.dtype, cu, SCALE, True, rows, heads, threads=8)
+    check_attention(got[rows, heads], ref, w.dtype, label="qwen full-size prefill (sampled)")
