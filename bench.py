@@ -150,7 +150,8 @@ def prefill_leg(torch, kivi, inputs, dev, n_iter: int, check: bool):
            "flop_per_launch": flop,
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "kernel": "prefill_kernel, one kivi_prefill_attention call"}}
+                        "kernel": "prefill_kernel, one kivi_prefill_attention call"},
+           "mfma_util_pct_pmc": measured_mfma_util(w.name)}
     if check:
         import oracle
         got = out.cpu().numpy().view(np.uint16)
@@ -182,6 +183,31 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _profile_values(path: str) -> dict:
+    vals = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def measured_mfma_util(workload: str):
+    """MFMA utilisation (%) of prefill_kernel from the committed rocprofv3 PMC summary,
+    if it was taken on the current kernel sources; else None."""
+    vals = _profile_values(os.path.join(ROOT, "profiles", "prefill_kernel_%s.txt" % workload))
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    for k, v in vals.items():
+        if k.startswith("MFMA utilisation"):
+            try:
+                return float(v.split()[0])
+            except ValueError:
+                return None
+    return None
 
 
 def measured_traffic(cfg_name: str):
