@@ -127,6 +127,13 @@ class Workload:
                 k[:, h, oc[h]] *= self.outlier_scale
         return to_bits(k, self.dtype), to_bits(v, self.dtype)
 
+    def kv_streams(self, threads: int = 8) -> list:
+        """kv_stream(s) for every request, drawn on a thread pool (numpy's generators
+        release the GIL while filling); identical to the serial calls."""
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            return list(ex.map(self.kv_stream, range(self.num_seqs)))
+
     def q_decode(self, step: int = 0) -> np.ndarray:
         """Decode queries for one step: [S][H_Q][d] uint16."""
         x = self._rng(2, step).standard_normal((self.num_seqs, self.num_q_heads, self.head_dim))

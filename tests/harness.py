@@ -162,6 +162,104 @@ def compare_seq_state(gpu: dict, orc: oracle.SeqCache, h: int, label: str = ""):
                                  f"gpu={g[tuple(bad[0])]} oracle={o[tuple(bad[0])]}")
 
 
+class PoolMirror:
+    """Host copy of a GPU pool, refreshed page by page: after a decode step only the
+    pages that step wrote (and the rings) are copied back."""
+
+    def __init__(self, gc: "GpuCache"):
+        self.gc = gc
+        gc.torch.cuda.synchronize()
+        self.host = gc.pool.cpu().numpy().copy()
+
+    def refresh(self, pages) -> None:
+        gc, L = self.gc, self.gc.layout
+        torch = gc.torch
+        H, nb = gc.w.num_kv_heads, gc.cfg.num_blocks
+        torch.cuda.synchronize()
+        pg = np.unique(np.asarray(pages, dtype=np.int64))
+        if pg.size:
+            idx = torch.from_numpy(pg).to(gc.device)
+            for key, per in (("k_codes", "code_bytes"), ("v_codes", "code_bytes"),
+                             ("k_meta", "k_meta_bytes"), ("v_meta", "v_meta_bytes")):
+                off, row = L[key], H * L[per]
+                dev2d = gc.pool[off:off + nb * row].view(nb, row)
+                self.host[off:off + nb * row].reshape(nb, row)[pg] = dev2d.index_select(0, idx).cpu().numpy()
+        n = gc.cfg.max_seqs * H * L["ring_bytes"]
+        for key in ("k_ring", "v_ring"):
+            off = L[key]
+            self.host[off:off + n] = gc.pool[off:off + n].cpu().numpy()
+
+
+def check_decode_step_state(mirror: PoolMirror, bt_np: np.ndarray, orcs: list, lens_before, lens_after,
+                            label: str = "") -> None:
+    """Bitwise check of everything one append step changed, for every request:
+    the Value page that received the evicted token (all its tokens so far), the Key
+    pages and metadata of a flushed residual, and the whole residual window."""
+    gc = mirror.gc
+    w = gc.w
+    L, b = gc.layout, mirror.host
+    H, R, G, Bk, bits = w.num_kv_heads, w.residual, w.k_group, w.block_size, w.bits
+    cb, mb, vmb = L["code_bytes"], L["k_meta_bytes"], L["v_meta_bytes"]
+    ng = D // w.v_group
+    nch = D * Bk // G
+    S = len(orcs)
+    ringK = b[L["k_ring"]:L["k_ring"] + gc.cfg.max_seqs * H * L["ring_bytes"]].view("<u2").reshape(-1, H, R, D)
+    ringV = b[L["v_ring"]:L["v_ring"] + gc.cfg.max_seqs * H * L["ring_bytes"]].view("<u2").reshape(-1, H, D, R)
+
+    def page_bytes(base, per, p):
+        return b[base + p * H * per: base + (p + 1) * H * per].reshape(H, per)
+
+    # Value: the page holding token TV_before (one evicted token per step)
+    v_seqs = [s for s in range(S) if max(0, lens_after[s] - R) > max(0, lens_before[s] - R)]
+    if v_seqs:
+        pages = np.array([bt_np[s, max(0, lens_before[s] - R) // Bk] for s in v_seqs])
+        chunks = np.stack([page_bytes(L["v_codes"], cb, p) for p in pages])  # [n][H][cb]
+        codes = decode_codes(chunks.reshape(-1, cb), bits, "v").reshape(len(v_seqs), H, Bk, D)
+        for i, s in enumerate(v_seqs):
+            a = orcs[s].arrays()
+            TV = max(0, lens_after[s] - R)
+            t0 = (TV - 1) // Bk * Bk
+            n = TV - t0
+            exp = a["v_code"][:, t0:TV]
+            if not np.array_equal(codes[i, :, :n], exp):
+                bad = np.argwhere(codes[i, :, :n] != exp)[0]
+                raise AssertionError(f"{label}: v_code seq {s} head {bad[0]} token {t0 + bad[1]} ch {bad[2]}")
+            meta = page_bytes(L["v_meta"], vmb, pages[i]).view("<u2").reshape(H, Bk, ng, 2)
+            for name, k in (("v_s", 0), ("v_z", 1)):
+                if not np.array_equal(meta[:, :n, :, k], a[name][:, t0:TV]):
+                    raise AssertionError(f"{label}: {name} seq {s} tokens {t0}..{TV}")
+    # Key flushes
+    for s in range(S):
+        tk0, tk1 = R * (lens_before[s] // R), R * (lens_after[s] // R)
+        if tk1 == tk0:
+            continue
+        a = orcs[s].arrays()
+        pages = bt_np[s, tk0 // Bk: tk1 // Bk]
+        chunks = np.stack([page_bytes(L["k_codes"], cb, p) for p in pages], axis=1)  # [H][np][cb]
+        for h in range(H):
+            got = decode_codes(chunks[h], bits, "k")
+            if not np.array_equal(got, a["k_code"][h, tk0:tk1]):
+                raise AssertionError(f"{label}: k_code seq {s} head {h} tokens {tk0}..{tk1}")
+        for jg in range(tk0 // G, tk1 // G):
+            for i in range(G // Bk):
+                raw = page_bytes(L["k_meta"], mb, bt_np[s, jg * G // Bk + i]).view("<u2")
+                for h in range(H):
+                    sl = slice(i * nch, (i + 1) * nch)
+                    if not (np.array_equal(raw[h, :nch], a["k_s"][h, jg, sl]) and
+                            np.array_equal(raw[h, nch:2 * nch], a["k_z"][h, jg, sl])):
+                        raise AssertionError(f"{label}: k meta seq {s} head {h} group {jg}")
+    # residual windows
+    for s in range(S):
+        T = int(lens_after[s])
+        TK, TV = R * (T // R), max(0, T - R)
+        a = orcs[s].arrays()
+        if T > TK and not np.array_equal(ringK[s][:, np.arange(TK, T) % R], a["k_raw"][:, TK:T]):
+            raise AssertionError(f"{label}: Key residual seq {s}")
+        if T > TV and not np.array_equal(np.swapaxes(ringV[s][:, :, np.arange(TV, T) % R], 1, 2),
+                                         a["v_raw"][:, TV:T]):
+            raise AssertionError(f"{label}: Value residual seq {s}")
+
+
 # ---------------------------------------------------------------------------
 # GPU cache driven through the C ABI
 # ---------------------------------------------------------------------------
