@@ -362,23 +362,28 @@ def main():
            torch.cuda.Event(enable_timing=True)) for _ in range(total)]
     step_bytes = []
 
-    def one_step(i):
+    def one_step(i, timed_parts=False):
+        # timed_parts (warm-up only): events around the append and the decode, for the
+        # split reported next to the result; the timed steps carry no event work
         r = i % n_rep
         h = handles[r]
         e0, e1, e2 = ev[i]
-        e0.record(stream)
+        if timed_parts:
+            e0.record(stream)
         kivi.kivi_append_tokens(h, S, slots, lens_before_dev[i], cu_one, 1, step_k[i], step_v[i], bt,
                                 bt.shape[1], stream)
-        e1.record(stream)
+        if timed_parts:
+            e1.record(stream)
         kivi.kivi_decode_attention(h, S, HQ, step_q[i], slots, lens_after_dev[i], max_len, bt, bt.shape[1],
                                    scale, out, ws, ws_bytes, stream)
-        e2.record(stream)
+        if timed_parts:
+            e2.record(stream)
         lens[r] += 1
         step_bytes.append(decode_bytes(lens[r], w))
 
     with torch.cuda.stream(stream):
         for i in range(n_warm):
-            one_step(i)
+            one_step(i, timed_parts=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n_warm, total):
@@ -386,24 +391,30 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     wall = t1 - t0
-    append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(n_warm, total)])
-    decode_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(n_warm, total)])
+    part_steps = range(min(2, n_warm), n_warm)  # warm-up steps with events (first two skipped)
+    append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in part_steps] or [float("nan")])
+    decode_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in part_steps] or [float("nan")])
 
     # ---- decode launches back to back (the kernel's own duration for the roofline): the host
-    # queues every call before the GPU drains them, so event gaps are kernel time ----
+    # queues every call before the GPU drains them; one event pair brackets the run, so the
+    # mean is kernel time plus the launch gap, with no event work between launches ----
     n_dec = n_steps
     dec_lens = [torch.from_numpy(lens[r].astype(np.int32)).to(dev) for r in range(n_rep)]
-    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec + 1)]
+    n_runs = 5
+    launch_ms = []
     with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        dev_ev[0].record(stream)
-        for i in range(n_dec):
-            r = i % n_rep
-            kivi.kivi_decode_attention(handles[r], S, HQ, step_q[i], slots, dec_lens[r],
-                                       max_len, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
-            dev_ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-    launch_ms = np.array([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(n_dec)])
+        for _ in range(n_runs):
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e_a.record(stream)
+            for i in range(n_dec):
+                r = i % n_rep
+                kivi.kivi_decode_attention(handles[r], S, HQ, step_q[i], slots, dec_lens[r],
+                                           max_len, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
+            e_b.record(stream)
+            torch.cuda.synchronize()
+            launch_ms.append(e_a.elapsed_time(e_b) / n_dec)
+    launch_ms = np.array(launch_ms)
     launch_bytes = float(np.mean([decode_bytes(lens[i % n_rep], w) for i in range(n_dec)]))
     timed_bytes = np.array(step_bytes[n_warm:], dtype=np.float64)
     timed_tokens = S * np.array([T0 + 1 + i // n_rep for i in range(n_warm, total)], dtype=np.float64)
@@ -432,10 +443,11 @@ def main():
                    "step": "append 1 token/request + split-K decode attention + merge"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": float(timed_tokens.sum() / wall),
-        "decode_us_mean": round(float(decode_ms.mean()) * 1e3, 2),
-        "decode_us_p10_p50_p90": [round(float(np.percentile(decode_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
-        "append_us_mean": round(float(append_ms.mean()) * 1e3, 2),
+        "warmup_step_split_us": {"append": round(float(append_ms.mean()) * 1e3, 2),
+                                 "decode": round(float(decode_ms.mean()) * 1e3, 2),
+                                 "note": "warm-up steps, each call bracketed by HIP events"},
         "decode_launch_us_mean": round(float(launch_ms.mean()) * 1e3, 2),
+        "decode_launch_us_runs": [round(float(x) * 1e3, 2) for x in launch_ms],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

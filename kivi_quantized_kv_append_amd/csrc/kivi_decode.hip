@@ -38,7 +38,7 @@ constexpr int kWaves = 8;
 // Value metadata of wide Value groups, and never more than the tiles of a
 // Key group (so at most one group begins inside a buffer).
 template <int NG>
-__host__ __device__ constexpr int max_buffer_tiles() { return NG == 1 ? 4 : (NG <= 4 ? 2 : 1); }
+__host__ __device__ constexpr int max_buffer_tiles() { return NG <= 2 ? 2 : 1; }
 
 struct DecodeArgs {
     CacheView v;
