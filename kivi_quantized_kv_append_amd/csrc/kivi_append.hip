@@ -84,6 +84,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         return canon(to_f32<DT>(u));
     };
 
+    // A one-row append (a decode step) loads its new row here, so the load
+    // travels with phase A's ring reads instead of after them.
+    const bool one_row = (n == 1);
+    uint4 row_k = {0, 0, 0, 0};
+    uint16_t row_v = 0;
+    if (one_row) {
+        if (tid < 16) row_k = *reinterpret_cast<const uint4*>(inK + 8 * tid);
+        if (tid < kHeadDim) row_v = inV[tid];
+    }
+
     __shared__ float sm_min[2][kHeadDim], sm_max[2][kHeadDim];
     __shared__ float sm_S[kHeadDim], sm_Z[kHeadDim];
     __shared__ uint8_t sm_codes[kMaxG * kHeadDim];
@@ -212,18 +222,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
                     return group_code(sm_v[wave][r][ch], sm_vp[wave][r][g][0], sm_vp[wave][r][g][1], QMAX);
                 };
                 bool in[4];
-                bool all = true;
-                for (int r = 0; r < 4; ++r) {
-                    in[r] = (p0 + r >= TV0) && (p0 + r < TV1);
-                    all = all && in[r];
-                }
+                for (int r = 0; r < 4; ++r) in[r] = (p0 + r >= TV0) && (p0 + r < TV1);
                 const int words = (BITS == 4) ? 64 : 32;
+                // The call that writes a quad's first token stores whole words
+                // (fields of later tokens zero); later calls OR their fields in,
+                // so no word is read back.
+                const bool fresh = p0 >= TV0;
                 if (blk >= 0 && lane < words) {
                     const int m = lane & 15, w = lane >> 4;
                     const int L = m + 16 * jq;
                     uint32_t* dst = reinterpret_cast<uint32_t*>(V.v_codes + ((size_t)blk * H + h) * V.code_bytes +
                                                                 sub * TILE_BYTES + SLOT_BYTES * L + 4 * w);
-                    uint32_t word = all ? 0u : *dst;
+                    uint32_t word = 0u;
                     if constexpr (BITS == 4) {
                         const int ca = 32 * w + m, cc = ca + 16;
                         // nibble e: (a,0) (a,2) (c,0) (c,2) (a,1) (a,3) (c,1) (c,3)
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
                         for (int e = 0; e < 8; ++e) {
                             const int r = etk[e];
                             if (!in[r]) continue;
-                            word = (word & ~(0xFu << (4 * e))) | (code_at(r, ech[e]) << (4 * e));
+                            word |= code_at(r, ech[e]) << (4 * e);
                         }
                     } else {
                         // field f (low half) = (tile 4w + f/2, token 2(f%2)); field 8+f = token + 1
@@ -241,10 +251,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
                             const int ch = 16 * (4 * w + ff / 2) + m;
                             const int r = 2 * (ff & 1) + (f >> 3);
                             if (!in[r]) continue;
-                            word = (word & ~(0x3u << (2 * f))) | (code_at(r, ch) << (2 * f));
+                            word |= code_at(r, ch) << (2 * f);
                         }
                     }
-                    *dst = word;
+                    if (fresh) *dst = word;
+                    else __hip_atomic_fetch_or(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             __syncthreads();
@@ -259,6 +270,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     {
         const int k_first = max(TK1, T0), v_first = max(TV1, T0);
         const int nk = T1 - k_first, nv = T1 - v_first;
+        if (one_row) {  // the row is at position T0 (nk, nv <= 1)
+            if (nk > 0 && tid < 16) *reinterpret_cast<uint4*>(ringK + (size_t)(T0 % R) * kHeadDim + 8 * tid) = row_k;
+            if (nv > 0 && tid < kHeadDim) ringV[(size_t)tid * R + (T0 % R)] = row_v;
+            return;
+        }
         // Key ring: token-major rows, 16-byte chunks
         for (int q = tid; q < nk * 16; q += kAppendThreads) {
             const int p = k_first + q / 16, ch = (q % 16) * 8;
