@@ -122,3 +122,74 @@ def test_decode_bf16_qwen_shape():
     got = gc.decode(q, SCALE)
     ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, [0, 1, 2], SCALE, False, threads=8)
     check_attention(got, ref, w.dtype, label="bf16 decode")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_constant_groups_bitexact(bits):
+    """Degenerate groups: Key channels constant over a whole Key group and Value
+    tokens whose channel groups are constant (zero scale, every code 0, the
+    value restored exactly from the zero-point), including all-zero groups."""
+    w = _variant(1, bits=bits, k_group=32, v_group=32, residual=64, num_kv_heads=2, num_q_heads=8,
+                 num_seqs=2, seq_lens=[300, 200], shuffle=True, pool_factor=1.5, n_outlier=2)
+    streams = []
+    for s in range(w.num_seqs):
+        k, v = w.kv_stream(s)
+        k, v = k.copy(), v.copy()
+        one = inputs.to_bits(np.array([0.75, -2.0, 0.0]), w.dtype)
+        k[32:64, :, 5] = one[0]      # one whole Key group of channel 5
+        k[64:96, 1, 9] = one[1]
+        k[96:128, :, 100] = one[2]
+        v[10:20, :, 0:32] = one[0]   # Value group 0 of tokens 10..19
+        v[40:44, 0, :] = one[2]      # every group of tokens 40..43, head 0
+        v[70, 1, 64:96] = one[1]
+        streams.append((k, v))
+    gc = GpuCache(w)
+    orc = [oracle_caches(w, lens=np.zeros(w.num_seqs, dtype=np.int64))[s] for s in range(w.num_seqs)]
+    pos = 0
+    for n in [1, 37, 64, 200]:
+        rk = [streams[s][0][pos:pos + n] for s in range(w.num_seqs)]
+        rv = [streams[s][1][pos:pos + n] for s in range(w.num_seqs)]
+        n_s = [min(n, int(w.seq_lens[s]) - pos) for s in range(w.num_seqs)]
+        rk = [r[:max(m, 0)] for r, m in zip(rk, n_s)]
+        rv = [r[:max(m, 0)] for r, m in zip(rv, n_s)]
+        gc.append(rk, rv)
+        for s in range(w.num_seqs):
+            orc[s].append(rk[s], rv[s])
+        pos += n
+    lens = np.minimum(pos, w.seq_lens)
+    pv = gc.pool_view()
+    for s in range(w.num_seqs):
+        a = orc[s].arrays()
+        for h in range(w.num_kv_heads):
+            compare_seq_state(pv.seq_state(gc.bt_np[s], s, int(lens[s]), h), orc[s], h, label=f"seq {s} head {h}")
+        # the planted groups did quantise to zero scale
+        assert np.all(a["k_s"][:, 1, 5] == 0) and np.all(a["v_s"][:, 10, 0] == 0)
+    q = w.q_decode(3)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False, threads=8)
+    check_attention(got, ref, w.dtype, label="constant groups decode")
+
+
+def test_llama_decode_full_size():
+    """The benchmark's decode workload at full size (32 requests x 4096 tokens, int4,
+    G = 64, R = 128, in-order pages), one appended token, every output against
+    the oracle; the cache state of two requests (all heads) bit for bit."""
+    w = inputs.config(2, extra_tokens=1)
+    S, T0 = w.num_seqs, int(w.seq_lens[0])
+    streams = w.kv_streams(16)
+    gc = GpuCache(w)
+    gc.append([st[0][:T0] for st in streams], [st[1][:T0] for st in streams])
+    gc.append([st[0][T0:T0 + 1] for st in streams], [st[1][T0:T0 + 1] for st in streams])
+    orc = []
+    for s in range(S):
+        c = oracle.SeqCache(w.num_kv_heads, 128, w.bits, w.k_group, w.v_group, w.residual, w.dtype, T0 + 1)
+        c.append(streams[s][0][:T0 + 1], streams[s][1][:T0 + 1])
+        orc.append(c)
+    pv = gc.pool_view()
+    for s in (0, S - 1):
+        for h in range(w.num_kv_heads):
+            compare_seq_state(pv.seq_state(gc.bt_np[s], s, T0 + 1, h), orc[s], h, label=f"seq {s} head {h}")
+    q = w.q_decode(0)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(S + 1), SCALE, False, threads=16)
+    check_attention(got, ref, w.dtype, label="llama full-size decode")

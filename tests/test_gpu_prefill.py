@@ -40,6 +40,7 @@ def test_prefill_ragged_chunks_int2():
                       residual=64, seq_lens=[150, 400, 37], extra_tokens=90, shuffle=True, pool_factor=1.5)
     _prefill_case(w, [90, 17, 1], causal=True)
     _prefill_case(w, [90, 17, 1], causal=False)
+    _prefill_case(w, [0, 17, 90], causal=True)  # a request with no rows in this call
 
 
 def test_prefill_chunk_longer_than_residual():
