@@ -458,6 +458,13 @@ def main():
         "parity": parity,
         "input_gen_s": round(gen_s, 1),
     }
+    # capacity of a 1 GiB per-layer budget in this workload's layout, against fp16 K/V
+    budget = 1 << 30
+    _, cap_tokens = kivi.kivi_cache_capacity(cfg, budget)
+    fp16_tokens = budget // (2 * H * d * 2)
+    res["capacity"] = {"budget_bytes": budget, "kv_tokens": cap_tokens, "fp16_kv_tokens": fp16_tokens,
+                       "density_vs_fp16": round(cap_tokens / fp16_tokens, 3),
+                       "note": f"one layer, {H} KV heads, residual rings for {S} sequences included"}
     for h in handles:
         kivi.kivi_cache_destroy(h)
     del pools, step_k, step_v, step_q

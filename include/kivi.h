@@ -145,6 +145,20 @@ typedef struct kivi_cache kivi_cache;
  * Errors: INVALID_ARG (null), UNSUPPORTED (see kivi_cache_config).            */
 kivi_status kivi_cache_pool_bytes(const kivi_cache_config* cfg, size_t* bytes);
 
+/* Capacity of a memory budget: the largest num_blocks whose pool (with
+ * cfg's other fields; cfg->num_blocks is ignored) fits in budget_bytes, and
+ * the tokens those pages hold (num_blocks * block_size, per layer, all KV
+ * heads). This is the density the product pages sell ("S4 KV": about three
+ * times the fp16 KV tokens per GPU for int4) and the M_KV estimate of
+ * "4.4 KV Cache 量化", section 1, with this layout's group metadata and
+ * residual rings included. Host only, no device work.
+ * A Key or Value code sub-array is limited to 4 GiB (32-bit page offsets),
+ * which caps num_blocks for very large budgets.
+ * Outputs: *num_blocks (0 when not even the rings fit), *kv_tokens.
+ * Errors: INVALID_ARG (null), UNSUPPORTED (as kivi_cache_pool_bytes).       */
+kivi_status kivi_cache_capacity(const kivi_cache_config* cfg, size_t budget_bytes, int32_t* num_blocks,
+                                int64_t* kv_tokens);
+
 /* Bind a cache to the caller's device pool. The caller allocates and owns
  * d_pool (256-byte aligned, at least kivi_cache_pool_bytes()) and frees it
  * after kivi_cache_destroy(). The handle holds host metadata only: no device

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <climits>
 #include <limits>
 #include <string>
 
@@ -180,6 +181,30 @@ kivi_status kivi_cache_pool_bytes(const kivi_cache_config* cfg, size_t* bytes) {
     if (L.total_bytes > (uint64_t)std::numeric_limits<size_t>::max())
         return fail(KIVI_ERR_UNSUPPORTED, "pool size overflows size_t");
     *bytes = (size_t)L.total_bytes;
+    return ok();
+}
+
+kivi_status kivi_cache_capacity(const kivi_cache_config* cfg, size_t budget_bytes, int32_t* num_blocks,
+                                int64_t* kv_tokens) {
+    if (!num_blocks || !kv_tokens) return fail(KIVI_ERR_INVALID_ARG, "output pointer is NULL");
+    if (!cfg) return fail(KIVI_ERR_INVALID_ARG, "config is NULL");
+    kivi_cache_config c = *cfg;
+    c.num_blocks = 1;
+    kivi_layout L;
+    kivi_status s = check_config(&c, &L);
+    if (s != KIVI_OK) return s;
+    // largest block count whose pool fits the budget (and the 4 GiB code sub-array)
+    const uint64_t H = (uint64_t)c.num_kv_heads;
+    int64_t lo = 0, hi = std::min<int64_t>(INT32_MAX, (int64_t)(((1ull << 32) - 1) / (H * L.code_bytes)));
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        c.num_blocks = (int32_t)mid;
+        kivi_layout M;
+        if (check_config(&c, &M) == KIVI_OK && M.total_bytes <= (uint64_t)budget_bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    *num_blocks = (int32_t)lo;
+    *kv_tokens = lo * (int64_t)c.block_size;
     return ok();
 }
 

@@ -28,7 +28,7 @@ KIVI_F16 = 0
 KIVI_BF16 = 1
 
 EXPORTED = [
-    "kivi_cache_pool_bytes", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
+    "kivi_cache_pool_bytes", "kivi_cache_capacity", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
     "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention",
     "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_last_error",
     "kivi_status_string",
@@ -71,6 +71,7 @@ def load():
         P, I32, S = c.c_void_p, c.c_int32, c.c_size_t
         CFG = c.POINTER(kivi_cache_config)
         L.kivi_cache_pool_bytes.argtypes = [CFG, c.POINTER(S)]
+        L.kivi_cache_capacity.argtypes = [CFG, S, c.POINTER(c.c_int32), c.POINTER(c.c_int64)]
         L.kivi_cache_create.argtypes = [CFG, P, S, c.POINTER(P)]
         L.kivi_cache_destroy.argtypes = [P]
         L.kivi_cache_destroy.restype = None
@@ -130,6 +131,13 @@ def kivi_cache_pool_bytes(cfg: kivi_cache_config) -> int:
     out = ctypes.c_size_t()
     _check(load().kivi_cache_pool_bytes(ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
+
+
+def kivi_cache_capacity(cfg: kivi_cache_config, budget_bytes: int):
+    """(num_blocks, kv_tokens) that fit in budget_bytes (cfg.num_blocks is ignored)."""
+    nb, tok = ctypes.c_int32(), ctypes.c_int64()
+    _check(load().kivi_cache_capacity(ctypes.byref(cfg), int(budget_bytes), ctypes.byref(nb), ctypes.byref(tok)))
+    return nb.value, tok.value
 
 
 def kivi_cache_create(cfg: kivi_cache_config, d_pool, pool_bytes: int) -> int:

@@ -43,6 +43,38 @@ def test_pool_bytes_matches_layout_formula():
     assert n == 2 * codes + kmeta + vmeta + 2 * ring
 
 
+@pytest.mark.parametrize("bits,budget", [(4, 1 << 30), (2, 1 << 30), (4, 70 << 30), (4, 3 << 20), (4, 1000)])
+def test_capacity_is_the_largest_pool_that_fits(bits, budget):
+    c = cfg(bits=bits)
+    nb, tokens = kivi.kivi_cache_capacity(c, budget)
+    assert tokens == nb * 16
+    if nb == 0:
+        assert kivi.kivi_cache_pool_bytes(cfg(bits=bits, num_blocks=1)) > budget
+        return
+    assert kivi.kivi_cache_pool_bytes(cfg(bits=bits, num_blocks=nb)) <= budget
+    try:
+        assert kivi.kivi_cache_pool_bytes(cfg(bits=bits, num_blocks=nb + 1)) > budget
+    except kivi.KiviError as e:  # one more block passes the 4 GiB code sub-array limit
+        assert e.status == kivi.KIVI_ERR_UNSUPPORTED and "4 GiB" in str(e)
+
+
+def test_capacity_density_against_fp16():
+    """Tokens per byte against an fp16 cache of the same budget, whose size is the
+    M_KV formula at 16 bits ("4.4 KV Cache 量化", section 1). The codes alone give
+    4x at int4 (8x at int2); group metadata and the residual rings take some of it
+    back. The product pages quote about 3x for their int4 backend."""
+    budget = 8 << 30
+    fp16_tokens = budget // oracle.m_kv_bytes(1, 1, 1, 8, 128, 16)
+    for bits, lo, hi in ((4, 3.0, 4.0), (2, 5.0, 8.0)):
+        _, tokens = kivi.kivi_cache_capacity(cfg(bits=bits, max_seqs=256), budget)
+        ratio = tokens / fp16_tokens
+        assert lo < ratio < hi, (bits, ratio)
+    # with Key groups of 64 tokens and 128-channel Value groups: codes 128 B, Key
+    # meta 8 B, Value meta 4 B per token and head, against 512 B in fp16
+    _, tokens = kivi.kivi_cache_capacity(cfg(bits=4, max_seqs=1), budget)
+    assert abs(tokens / fp16_tokens - 512 / 140) < 0.01
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_code_payload_equals_m_kv(bits):
     """The code sub-arrays hold exactly M_KV = 2 L B T H_KV d b bytes for the tokens their
