@@ -225,26 +225,36 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             f4 ra = code_scores<BITS>(ta.k, lt, lane_row, bias);
             f4 rb = ra;
             if (kPair) rb = code_scores<BITS>(tb.k, lt, lane_row, bias);
-            // visibility of token 16 t' + 4 j + r to this lane's row
-            bool va[4], vb[4];
-            const bool full_a = t < full_tiles, full_b = t + 1 < full_tiles;  // uniform
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                va[r] = oka && (full_a || 16 * t + 4 * j + r <= my_last);
-                vb[r] = okb && (full_b || 16 * (t + 1) + 4 * j + r <= my_last);
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (va[r]) mx = max2(mx, ra[r]);
-                if (vb[r]) mx = max2(mx, rb[r]);
-            }
-            st.rescale(xor_max(mx), sl2, thr);
             float pa[4], pb[4];
+            if (oka && okb && t + 1 < full_tiles) {  // both tiles seen whole by every row (uniform)
+                const float mx = max2(max4(ra), max4(rb));
+                st.rescale(xor_max(mx), sl2, thr);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pa[r] = va[r] ? st.weight(ra[r], sl2) : 0.0f;
-                pb[r] = vb[r] ? st.weight(rb[r], sl2) : 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    pa[r] = st.weight(ra[r], sl2);
+                    pb[r] = st.weight(rb[r], sl2);
+                }
+            } else {
+                // visibility of token 16 t' + 4 j + r to this lane's row
+                bool va[4], vb[4];
+                const bool full_a = t < full_tiles, full_b = t + 1 < full_tiles;  // uniform
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    va[r] = oka && (full_a || 16 * t + 4 * j + r <= my_last);
+                    vb[r] = okb && (full_b || 16 * (t + 1) + 4 * j + r <= my_last);
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (va[r]) mx = max2(mx, ra[r]);
+                    if (vb[r]) mx = max2(mx, rb[r]);
+                }
+                st.rescale(xor_max(mx), sl2, thr);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pa[r] = va[r] ? st.weight(ra[r], sl2) : 0.0f;
+                    pb[r] = vb[r] ? st.weight(rb[r], sl2) : 0.0f;
+                }
             }
             st.l_acc += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
             value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb);
