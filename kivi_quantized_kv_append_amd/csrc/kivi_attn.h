@@ -96,23 +96,24 @@ __device__ __forceinline__ uint2 buf_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // int4: word i covers channels 32i+8j..+7 (even in the low half, odd in the
 // high half), pair factors 1,16,1,16. int2: word w covers MFMAs 2w (fields
 // 0..3) and 2w+1 (fields 4..7), pair factors 1,4,16,64.
-template <int BITS>
+// kFold: keep the 1024 offsets (one and-or per pair, no subtract); the table
+// built with the same kFold takes 1024 sum_c Q'[n][c] out of the bias instead.
+template <int BITS, bool kFold = false>
 __device__ __forceinline__ void unpack_k(const uint32_t* kw, h8 A[4]) {
+    auto pr = [](uint32_t x, uint32_t m) -> uint32_t { return kFold ? magic_pair(x, m) : exact_pair(x, m); };
     if constexpr (BITS == 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t w = kw[i], w8 = w >> 8;
-            A[i] = make_h8(exact_pair(w, 0x000F000Fu), exact_pair(w, 0x00F000F0u),
-                           exact_pair(w8, 0x000F000Fu), exact_pair(w8, 0x00F000F0u));
+            A[i] = make_h8(pr(w, 0x000F000Fu), pr(w, 0x00F000F0u), pr(w8, 0x000F000Fu), pr(w8, 0x00F000F0u));
         }
     } else {
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const uint32_t x = kw[w], x8 = x >> 8;
-            A[2 * w] = make_h8(exact_pair(x, 0x00030003u), exact_pair(x, 0x000C000Cu),
-                               exact_pair(x, 0x00300030u), exact_pair(x, 0x00C000C0u));
-            A[2 * w + 1] = make_h8(exact_pair(x8, 0x00030003u), exact_pair(x8, 0x000C000Cu),
-                                   exact_pair(x8, 0x00300030u), exact_pair(x8, 0x00C000C0u));
+            A[2 * w] = make_h8(pr(x, 0x00030003u), pr(x, 0x000C000Cu), pr(x, 0x00300030u), pr(x, 0x00C000C0u));
+            A[2 * w + 1] = make_h8(pr(x8, 0x00030003u), pr(x8, 0x000C000Cu), pr(x8, 0x00300030u),
+                                   pr(x8, 0x00C000C0u));
         }
     }
 }
@@ -194,7 +195,7 @@ __device__ __forceinline__ uint32_t k_meta_off(const CacheView& V, int h, int pa
 // Lane (k = lane & 15, r = lane >> 4) covers channels 8k..8k+7 of heads
 // r, r+4, r+8, r+12. sv/zv: the lane's 8 scales and zero-points. Returns
 // bias[nr] for this lane's score row nr: the start of its score chains.
-template <int BITS>
+template <int BITS, bool kFold = false>
 __device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const uint16_t* lq, uint8_t* lt, float* lbias,
                                              int nr, float sgn) {
     const int lane = threadIdx.x & 63, k = lane & 15, r = lane >> 4;
@@ -214,7 +215,8 @@ __device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const ui
         const uint4 qu = *reinterpret_cast<const uint4*>(lq + (ok ? hn : 0) * kQRow + 8 * k);
         const uint32_t qw[4] = {qu.x, qu.y, qu.z, qu.w};
         uint32_t hw[4], lw[4];
-        float zq = 0.0f;
+        float zq = 0.0f, qs = 0.0f;
+        const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const h2 qv = __builtin_bit_cast(h2, qw[e]);
@@ -223,12 +225,17 @@ __device__ __forceinline__ float build_table(int g, uint4 sv, uint4 zv, const ui
             hw[e] = __builtin_bit_cast(uint32_t, hi);
             lw[e] = __builtin_bit_cast(uint32_t, lo);
             zq = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2, zw[e]), zq, false);
+            if constexpr (kFold) {  // the table entries exactly as the MFMAs multiply them
+                qs = __builtin_amdgcn_fdot2(hi, one, qs, false);
+                qs = __builtin_amdgcn_fdot2(lo, one, qs, false);
+            }
         }
         zq = row_sum16(ok ? zq : 0.0f);
+        if constexpr (kFold) qs = row_sum16(ok ? qs : 0.0f);
         if (ok) {
             *reinterpret_cast<uint4*>(lt + (2 * hn + 0) * kRowBytes + 16 * k) = (uint4){hw[0], hw[1], hw[2], hw[3]};
             *reinterpret_cast<uint4*>(lt + (2 * hn + 1) * kRowBytes + 16 * k) = (uint4){lw[0], lw[1], lw[2], lw[3]};
-            if (k == 0) lbias[hn] = sgn * zq;
+            if (k == 0) lbias[hn] = kFold ? __builtin_fmaf(-1024.0f, qs, sgn * zq) : sgn * zq;
         }
     }
     // LDS operations of one wave complete in order; the fence keeps the
@@ -324,10 +331,10 @@ constexpr int flush_period() { return 16 / kHalf > 0 ? 16 / kHalf : 1; }
 // chain that starts at the zero-point bias and takes the group's hi and lo
 // B-operands from the wave's LDS table. `row`: the lane's byte offset into
 // the table (head row nr, k-slice 16 j).
-template <int BITS>
+template <int BITS, bool kFold = false>
 __device__ __forceinline__ f4 code_scores(const uint32_t* kw, const uint8_t* lt, int row, float bias) {
     h8 A[4];
-    unpack_k<BITS>(kw, A);
+    unpack_k<BITS, kFold>(kw, A);
     f4 acc = {bias, bias, bias, bias};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

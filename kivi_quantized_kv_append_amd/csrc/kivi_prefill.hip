@@ -26,6 +26,9 @@ using namespace attn;
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kRowsPerWave = 16;
+// Main-loop Key codes keep their 1024 offsets, taken out through the table's
+// bias (saves a packed subtract per code pair); the tail stays exact.
+constexpr bool kFoldK = true;
 
 struct PrefillArgs {
     CacheView v;
@@ -219,12 +222,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             constexpr bool kPair = kHalf > 1;
             const bool oka = b.ok[e], okb = kPair ? b.ok[kPair ? e + 1 : e] : false;
             if (!oka && !okb) continue;
-            if ((t & (tpg - 1)) == 0 && t != 0) bias = build_table<BITS>(kRowsPerWave, b.ms, b.mz, lq, lt, lbias, n, sgn);
+            if ((t & (tpg - 1)) == 0 && t != 0) bias = build_table<BITS, kFoldK>(kRowsPerWave, b.ms, b.mz, lq, lt, lbias, n, sgn);
             const TileRegs<BITS, NG>& ta = b.t[e];
             const TileRegs<BITS, NG>& tb = b.t[kPair ? e + 1 : e];
-            f4 ra = code_scores<BITS>(ta.k, lt, lane_row, bias);
+            f4 ra = code_scores<BITS, kFoldK>(ta.k, lt, lane_row, bias);
             f4 rb = ra;
-            if (kPair) rb = code_scores<BITS>(tb.k, lt, lane_row, bias);
+            if (kPair) rb = code_scores<BITS, kFoldK>(tb.k, lt, lane_row, bias);
             float pa[4], pb[4];
             if (oka && okb && t + 1 < full_tiles) {  // both tiles seen whole by every row (uniform)
                 const float mx = max2(max4(ra), max4(rb));
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         const uint32_t mo = k_meta_off(V, h, mp, nch);
         const uint4 ms0 = buf_b128(rkm, mo, 0);
         const uint4 mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
-        bias = build_table<BITS>(kRowsPerWave, ms0, mz0, lq, lt, lbias, n, sgn);
+        bias = build_table<BITS, kFoldK>(kRowsPerWave, ms0, mz0, lq, lt, lbias, n, sgn);
         int it = 0;
         for (int t0 = 0; t0 < m_end; t0 += 2 * kHalf) {
             issue(t0 + kHalf, bb);
