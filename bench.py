@@ -3,7 +3,9 @@
 A step is the decode hot path over one batch: append one new fp16 K/V token
 per request (Value eviction and quantisation, Key flush when a residual
 fills, residual write) and then split-K paged decode attention over the
-quantised cache plus residual, with the cross-split merge.
+quantised cache plus residual, with the cross-split merge: one
+kivi_decode_step call (--separate-calls: kivi_append_tokens then
+kivi_decode_attention).
 
 Workload: Llama-3-8B-shaped decode layer, 32 requests x 4096 cached tokens,
 32 query / 8 KV heads, head_dim 128, int4 (Key per-channel G=64, Value
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="0 = size for ~10-30 s")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time the step as kivi_append_tokens + kivi_decode_attention instead of kivi_decode_step")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the timed steps "
@@ -370,12 +374,18 @@ def main():
         e0, e1, e2 = ev[i]
         if timed_parts:
             e0.record(stream)
-        kivi.kivi_append_tokens(h, S, slots, lens_before_dev[i], cu_one, 1, step_k[i], step_v[i], bt,
-                                bt.shape[1], stream)
-        if timed_parts:
-            e1.record(stream)
-        kivi.kivi_decode_attention(h, S, HQ, step_q[i], slots, lens_after_dev[i], max_len, bt, bt.shape[1],
-                                   scale, out, ws, ws_bytes, stream)
+        if args.separate_calls:
+            kivi.kivi_append_tokens(h, S, slots, lens_before_dev[i], cu_one, 1, step_k[i], step_v[i], bt,
+                                    bt.shape[1], stream)
+            if timed_parts:
+                e1.record(stream)
+            kivi.kivi_decode_attention(h, S, HQ, step_q[i], slots, lens_after_dev[i], max_len, bt, bt.shape[1],
+                                       scale, out, ws, ws_bytes, stream)
+        else:
+            kivi.kivi_decode_step(h, S, HQ, step_q[i], slots, lens_before_dev[i], step_k[i], step_v[i], max_len,
+                                  bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
+            if timed_parts:
+                e1.record(stream)
         if timed_parts:
             e2.record(stream)
         lens[r] += 1
@@ -388,9 +398,11 @@ def main():
         t0 = time.perf_counter()
         for i in range(n_warm, total):
             one_step(i)
+        t_issued = time.perf_counter()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     wall = t1 - t0
+    host_issue_us = (t_issued - t0) * 1e6 / n_steps
     part_steps = range(min(2, n_warm), n_warm)  # warm-up steps with events (first two skipped)
     append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in part_steps] or [float("nan")])
     decode_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in part_steps] or [float("nan")])
@@ -440,12 +452,17 @@ def main():
         "config": {"workload": w0.name, "num_seqs": S, "seq_len": T0, "q_heads": HQ, "kv_heads": H,
                    "head_dim": d, "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
                    "residual": w.residual, "block_size": w.block_size, "replicas": n_rep,
-                   "step": "append 1 token/request + split-K decode attention + merge"},
+                   "step": ("kivi_append_tokens (1 token/request) + kivi_decode_attention (split-K decode + merge)"
+                            if args.separate_calls else
+                            "kivi_decode_step: append 1 token/request (evict, flush, residual) + split-K decode "
+                            "attention in one launch (+ merge when split)")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": float(timed_tokens.sum() / wall),
-        "warmup_step_split_us": {"append": round(float(append_ms.mean()) * 1e3, 2),
-                                 "decode": round(float(decode_ms.mean()) * 1e3, 2),
-                                 "note": "warm-up steps, each call bracketed by HIP events"},
+        "host_issue_us_per_step": round(host_issue_us, 2),
+        "warmup_step_split_us": ({"append": round(float(append_ms.mean()) * 1e3, 2),
+                                  "decode": round(float(decode_ms.mean()) * 1e3, 2)} if args.separate_calls else
+                                 {"decode_step": round(float(append_ms.mean()) * 1e3, 2)}) |
+                                {"note": "warm-up steps, each call bracketed by HIP events"},
         "decode_launch_us_mean": round(float(launch_ms.mean()) * 1e3, 2),
         "decode_launch_us_runs": [round(float(x) * 1e3, 2) for x in launch_ms],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

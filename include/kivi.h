@@ -222,6 +222,24 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
                                   float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
                                   void* stream);
 
+/* One decode step in one launch: append one token per sequence (as
+ * kivi_append_tokens with one row each: the Value eviction, the Key flush
+ * when the residual fills, the residual write; "4.4 KV Cache 量化", section
+ * 3.2) and then attend with that token's query over the sequence's T + 1
+ * tokens (as kivi_decode_attention). The cache state and the outputs are
+ * those of the two calls in a row.
+ *   d_seq_lens_before[S]  tokens before this step (the query sits at position T)
+ *   d_k_new, d_v_new      [S][H_KV][128] kv_dtype, row s is sequence s's token
+ *   max_seq_len           host upper bound of d_seq_lens_before + 1 (also
+ *                         for kivi_decode_workspace_bytes)
+ * Other arguments as kivi_decode_attention; slot ids must be distinct.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
+kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads, const void* d_q,
+                             const int32_t* d_slot_ids, const int32_t* d_seq_lens_before, const void* d_k_new,
+                             const void* d_v_new, int32_t max_seq_len, const int32_t* d_block_table,
+                             int32_t bt_stride, float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
+                             void* stream);
+
 /* Workspace bytes kivi_prefill_attention needs (0 today; reserved).          */
 kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
                                          int32_t num_q_heads, int32_t max_q_len,

@@ -24,7 +24,17 @@
 // fp16 mantissa under the exponent of 1024); Key codes also get a packed
 // subtract so they are exact integers. Query heads of a KV head (GQA) are
 // the matrix N dimension (<= 16).
+//
+// Fused decode step (kivi_decode_step): the same kernel first appends one
+// token per sequence. In split 0 of each (sequence, KV head), wave 7
+// quantises the Value token that leaves the window and writes the residual,
+// and, when the Key residual fills, waves 5 and 6 quantise its Key groups;
+// all of this runs beside the other waves' attention. Main tiles lie below
+// the old Value boundary, so the append writes nothing they read; the tile
+// of the evicted token is read by the wave that wrote it, and a flush step
+// reads its tail tiles after a barrier.
 
+#include "kivi_append_body.h"
 #include "kivi_attn.h"
 
 namespace kivi {
@@ -37,6 +47,7 @@ constexpr int kWaves = 8;
 // Main tiles of a SIMD's older wave, in percent of an even split (the
 // younger wave takes 200 minus this): measured best at 130 on MI355X.
 constexpr int kOldShare = 130;
+constexpr int kAppendShare = 70;  // main-tile share of the appending wave (20-70 measure alike)
 // Tiles per load buffer (two buffers per wave): deeper for the lighter
 // Value metadata of wide Value groups, and never more than the tiles of a
 // Key group (so at most one group begins inside a buffer).
@@ -59,6 +70,11 @@ struct DecodeArgs {
     int tpp_shift;    // log2(tiles per page)
     uint32_t code_array_bytes, vmeta_array_bytes, kmeta_array_bytes;
     uint16_t* out;
+    // Fused decode step: seq_lens holds the lengths before this step's token;
+    // split 0 of each (sequence, KV head) appends the token (rows of app.k_new
+    // / app.v_new in sequence order) before it attends over T + 1 tokens.
+    int fuse;
+    AppendArgs app;
 };
 
 // Per-wave LDS (dynamic shared memory, one region per wave), fp16 rows of
@@ -81,13 +97,16 @@ __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
     c.s = s;
     c.h = h;
     c.g = a.gqa;
-    int T = a.seq_lens[s];
+    const int T_in = a.seq_lens[s];
+    int T = T_in + a.fuse;
     c.slot = a.slot_ids[s];
-    if (c.slot < 0 || c.slot >= V.max_seqs || T < 0) T = 0;
+    if (c.slot < 0 || c.slot >= V.max_seqs || T_in < 0) T = 0;
     c.T = T;
     c.TK = V.R * (T / V.R);
     c.TV = max(0, T - V.R);
-    c.n_main = c.TV / kTile;
+    // main tiles: Key and Value both quantised before this call (a fused step
+    // writes only at or past the old Value boundary)
+    c.n_main = max(0, T - a.fuse - V.R) / kTile;
     c.bt = a.block_table + (size_t)s * a.bt_stride;
     c.bt_len = a.bt_stride;
     return c;
@@ -201,17 +220,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // main range: contiguous per wave, in split-major order. Waves 0-3 (one
     // per SIMD, dispatched first) win issue over waves 4-7 on their SIMD, so
     // they take the larger share and the pair ends together.
+    // In a fused step the last wave also appends, so it takes kAppendShare
+    // and waves 4-6 share the rest of the younger half.
+    auto weight = [&](int wv) -> int {
+        if (wv < 4) return 3 * kOldShare;
+        if (!a.fuse) return 3 * (200 - kOldShare);
+        return wv == kWaves - 1 ? 3 * kAppendShare : 4 * (200 - kOldShare) - kAppendShare;
+    };
     auto slot_start = [&](int ws) -> int {
         const int sp = ws / kWaves, wv = ws % kWaves;
-        const long long before = (long long)sp * kWaves * 100 + (wv < 4 ? wv * kOldShare : 4 * kOldShare + (wv - 4) * (200 - kOldShare));
-        return (int)((before * c.n_main) / ((long long)nslots * 100));
+        long long before = (long long)sp * kWaves * 300;
+        for (int w = 0; w < wv; ++w) before += weight(w);
+        return (int)((before * c.n_main) / ((long long)nslots * 300));
     };
     const int wslot = split * kWaves + wave;
     const int m_begin = slot_start(wslot);
     const int m_end = slot_start(wslot + 1);
     const int n_tail = (T + kTile - 1) / kTile - c.n_main;
-    const int tail_rank = wave * nvalid + split;  // tail tiles: rank, rank + nslots, ...
-    const int my_tail = n_tail > tail_rank ? (n_tail - tail_rank + nslots - 1) / nslots : 0;
+    // tail tiles: rank, rank + step, ...; a fused step leaves them to split 0,
+    // the work group that wrote them
+    // Fused step (split 0 only): without a Key flush only the tile of the
+    // Value token leaving the window (t_evict) depends on the append; the
+    // appending wave takes it, the other waves the rest in the prologue. A
+    // flush step takes every tail tile after a barrier at the end.
+    const bool flush_step = a.fuse && T > 0 && T % R == 0;  // uniform
+    const int t_evict = (a.fuse && T - 1 >= R) ? (T - 1 - R) / kTile : -1;
+    const bool skip_evict = a.fuse && !flush_step && t_evict >= 0;
+    const int n_tail_dealt = n_tail - (skip_evict ? 1 : 0);
+    int tail_step, tail_rank;
+    if (!a.fuse) {
+        tail_step = nslots;
+        tail_rank = wave * nvalid + split;
+    } else if (split != 0 || (!flush_step && wave == kWaves - 1)) {
+        tail_step = kWaves;
+        tail_rank = n_tail_dealt;  // none
+    } else {
+        tail_step = flush_step ? kWaves : kWaves - 1;
+        tail_rank = wave;
+    }
+    const int my_tail = n_tail_dealt > tail_rank ? (n_tail_dealt - tail_rank + tail_step - 1) / tail_step : 0;
+    auto tail_tile = [&](int k) -> int { return c.n_main + k + ((skip_evict && c.n_main + k >= t_evict) ? 1 : 0); };
 
     uint8_t* wl = smem + wave * wave_lds_bytes(g);
     uint16_t* lq = reinterpret_cast<uint16_t*>(wl);
@@ -233,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int base0 = (m_begin >> a.tpg_shift) << a.tpg_shift;  // windows start on a group
     int my_page = page_of_tile(a, c, base0 + lane);
     int next_page = page_of_tile(a, c, base0 + 64 + lane);
-    const int tail0 = c.n_main + tail_rank;
+    const int tail0 = tail_tile(tail_rank);
     const int tail_base0 = (tail0 >> a.tpg_shift) << a.tpg_shift;
     int tail_page = my_tail > 0 ? page_of_tile(a, c, tail_base0 + lane) : -1;
     load_query<DT>(a, c, lq);
@@ -270,9 +318,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             x.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
         } else {
             const int pk = min(p0 + n, T - 1);  // A row: token n of the tile
+            // a fused step's own token comes from its input row
+            const uint16_t* krow = (a.fuse && pk == T - 1)
+                                       ? a.app.k_new + ((size_t)c.s * H + c.h) * kHeadDim
+                                       : ringK + (size_t)(pk % R) * kHeadDim;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                x.kr[i] = *reinterpret_cast<const uint4*>(ringK + (size_t)(pk % R) * kHeadDim + 32 * i + 8 * j);
+            for (int i = 0; i < 4; ++i) x.kr[i] = *reinterpret_cast<const uint4*>(krow + 32 * i + 8 * j);
         }
         if (p0 < TV) {
             if constexpr (BITS == 4) {
@@ -294,6 +345,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
             x.vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
+        if (a.fuse && pq <= T - 1 && T - 1 < pq + 4) {  // a fused step's own token from its input row
+            const uint16_t* vrow = a.app.v_new + ((size_t)c.s * H + c.h) * kHeadDim;
+            const int r = T - 1 - pq, sh16 = 16 * (r & 1);
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                const uint32_t val = vrow[16 * tt + n];
+                if (r < 2) x.vr[tt].x = (x.vr[tt].x & ~(0xFFFFu << sh16)) | (val << sh16);
+                else x.vr[tt].y = (x.vr[tt].y & ~(0xFFFFu << sh16)) | (val << sh16);
+            }
+        }
     };
     auto tail_compute = [&](int t, const TailRegs<BITS, NG>& x) {
         if (x.blk < 0) return;
@@ -442,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // tiles hold many registers, finish the tail first) ----
     auto run_tail = [&]() {
         for (int i = 0; i < my_tail; ++i) {
-            const int t = tail0 + i * nslots;
+            const int t = tail_tile(tail_rank + i * tail_step);
             if (i > 0) {
                 const int tb = (t >> a.tpg_shift) << a.tpg_shift;
                 tail_page = page_of_tile(a, c, tb + lane);
@@ -452,7 +513,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             tail_compute(t, x);
         }
     };
-    if constexpr (NG >= 4) run_tail();
+    if constexpr (NG >= 4) {
+        if (!flush_step) run_tail();
+    }
     // buffers start a multiple of kHalf tiles after the window base, so
     // window boundaries fall between buffers (tiles before m_begin may ride
     // along, not computed)
@@ -466,7 +529,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         ms0 = buf_b128(rkm, mo, 0);
         mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
     }
-    if constexpr (NG < 4) run_tail();
+    if constexpr (NG < 4) {
+        if (!flush_step) run_tail();
+    }
+    // Fused step: split 0 appends this step's token with three waves while the
+    // others stream (wave 7: Value eviction and residual writes; waves 5 and 6:
+    // the Key flush when the residual fills). Main tiles lie below the old
+    // Value boundary, so nothing they read is written here.
+    if (a.fuse && split == 0) {
+        if (wave == kWaves - 1) {
+            append_token_value_wave<BITS, DT>(a.app, c.s, c.h, lane);
+            if (skip_evict) {  // the tile it just wrote: its own stores complete first
+                __builtin_amdgcn_s_waitcnt(0);
+                const int tb = (t_evict >> a.tpg_shift) << a.tpg_shift;
+                const int tpage = page_of_tile(a, c, tb + lane);
+                TailRegs<BITS, NG> x;
+                tail_issue(t_evict, tpage, x);
+                tail_compute(t_evict, x);
+            }
+        } else if (wave >= kWaves - 3) {
+            uint8_t* scratch = smem + kWaves * wave_lds_bytes(g) + (wave - (kWaves - 3)) * kMaxG * 64;
+            append_token_key_wave<BITS, DT>(a.app, c.s, c.h, wave - (kWaves - 3), lane, scratch);
+        }
+    }
     if (m_begin < m_end) {
         bias = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
         int it = 0;
@@ -483,6 +568,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     }
 
+    if (flush_step) {
+        // the append's stores complete, then split 0 takes the tail tiles,
+        // which hold what it wrote (the step's own token comes from its row)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        run_tail();
+    }
     // ---------------- merge the waves in LDS ----------------
     {
         const float l_tot = xor_sum(st.l_acc);
@@ -602,11 +694,49 @@ void launch_bits_dt(const DecodeArgs& a, int ng, int tpg, dim3 grid, size_t lds,
 
 }  // namespace
 
+namespace {
+int launch_decode_args(DecodeArgs& a, const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
+                       int bt_stride, float softmax_scale, void* out, float* partials,
+                       const DecodePlan& plan, size_t lds, void* stream);
+}  // namespace
+
 int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                   const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
                   int bt_stride, float softmax_scale, void* out, float* partials,
                   const DecodePlan& plan, void* stream) {
-    DecodeArgs a;
+    DecodeArgs a{};
+    a.fuse = 0;
+    return launch_decode_args(a, v, num_seqs, num_q_heads, q, slot_ids, seq_lens, block_table, bt_stride,
+                              softmax_scale, out, partials, plan, plan.lds_bytes, stream);
+}
+
+int launch_decode_step(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* slot_ids, const int32_t* seq_lens_before, const void* k_new,
+                       const void* v_new, const int32_t* block_table, int bt_stride, float softmax_scale,
+                       void* out, float* partials, const DecodePlan& plan, void* stream) {
+    DecodeArgs a{};
+    a.fuse = 1;
+    a.app.v = v;
+    a.app.slot_ids = slot_ids;
+    a.app.seq_lens_before = seq_lens_before;
+    a.app.cu_new = nullptr;  // one row per sequence, in sequence order
+    a.app.k_new = static_cast<const uint16_t*>(k_new);
+    a.app.v_new = static_cast<const uint16_t*>(v_new);
+    a.app.block_table = block_table;
+    a.app.bt_stride = bt_stride;
+    a.app.mode = 0;
+    const size_t lds = std::max(plan.lds_bytes, (size_t)kWaves * wave_lds_bytes(num_q_heads / v.H) +
+                                                    2 * (size_t)kMaxG * 64);  // + Key-flush scratch
+    return launch_decode_args(a, v, num_seqs, num_q_heads, q, slot_ids, seq_lens_before, block_table, bt_stride,
+                              softmax_scale, out, partials, plan, lds, stream);
+}
+
+namespace {
+int launch_decode_args(DecodeArgs& a, const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
+                       int bt_stride, float softmax_scale, void* out, float* partials,
+                       const DecodePlan& plan, size_t lds, void* stream) {
     a.v = v;
     a.q = static_cast<const uint16_t*>(q);
     a.slot_ids = slot_ids;
@@ -627,7 +757,6 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int ng = kHeadDim / v.Gv;
     dim3 grid((unsigned)(num_seqs * v.H * plan.n_splits));
-    const size_t lds = plan.lds_bytes;
     const int tpg = v.G / kTile;
     if (v.bits == 4) {
         if (v.dtype == kF16) launch_bits_dt<4, kF16>(a, ng, tpg, grid, lds, st);
@@ -643,6 +772,7 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
     }
     return (int)hipGetLastError();
 }
+}  // namespace
 
 size_t decode_lds_bytes(int g) {
     return std::max((size_t)kWaves * wave_lds_bytes(g), (size_t)merge_lds_bytes(g));

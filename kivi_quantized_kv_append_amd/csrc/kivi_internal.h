@@ -61,6 +61,13 @@ int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
                   const void* k_new, const void* v_new, const int32_t* block_table, int bt_stride,
                   void* stream);
 
+// Append one token per sequence and attend, in one launch (plus the merge
+// when sequences are split). seq_lens_before: lengths before the token.
+int launch_decode_step(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* slot_ids, const int32_t* seq_lens_before, const void* k_new,
+                       const void* v_new, const int32_t* block_table, int bt_stride, float softmax_scale,
+                       void* out, float* partials, const DecodePlan& plan, void* stream);
+
 int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                   const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
                   int bt_stride, float softmax_scale, void* out, float* partials,

@@ -336,6 +336,24 @@ class GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16)
 
+    def decode_step(self, k_rows: np.ndarray, v_rows: np.ndarray, q_bits: np.ndarray, scale: float):
+        """One fused step through kivi_decode_step: rows [S][H][128] (one new token per
+        sequence, all sequences), then attention with q over the new lengths."""
+        torch = self.torch
+        S, HQ = self.w.num_seqs, self.w.num_q_heads
+        q = self.t(np.ascontiguousarray(q_bits).view(np.int16))
+        dk = self.t(np.ascontiguousarray(k_rows).view(np.int16))
+        dv = self.t(np.ascontiguousarray(v_rows).view(np.int16))
+        out = torch.zeros((S, HQ, D), dtype=torch.int16, device=self.device)
+        msl = int(self.lens.max()) + 1
+        ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, S, HQ, msl)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        kivi.kivi_decode_step(self.handle, S, HQ, q, self.slots, self.t(self.lens.astype(np.int32)), dk, dv, msl,
+                              self.bt, self.bt.shape[1], scale, out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        self.lens += 1
+        return out.cpu().numpy().view(np.uint16)
+
     def prefill(self, q_bits: np.ndarray, cu_q: np.ndarray, scale: float, causal=True, seqs=None):
         torch = self.torch
         seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)

@@ -1,0 +1,66 @@
+"""GPU parity of the fused decode step (kivi_decode_step: append one token per
+sequence, then attend, in one launch) through the C ABI: after every step the
+whole cache state bit for bit against the oracle and against a second cache
+driven by the two separate calls, and the outputs against the oracle."""
+import numpy as np
+import pytest
+
+from kivi_quantized_kv_append_amd import inputs
+from harness import SCALE, GpuCache, check_attention, compare_seq_state, oracle_caches
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, steps, check_every=1):
+    S = w.num_seqs
+    streams = [w.kv_stream(s) for s in range(S)]
+    T0 = w.seq_lens.astype(np.int64)
+    fused, split = GpuCache(w), GpuCache(w)
+    for gc in (fused, split):
+        gc.append([streams[s][0][:T0[s]] for s in range(S)], [streams[s][1][:T0[s]] for s in range(S)])
+    orcs = oracle_caches(w)
+    for step in range(steps):
+        pos = T0 + step
+        k = np.stack([streams[s][0][pos[s]] for s in range(S)])
+        v = np.stack([streams[s][1][pos[s]] for s in range(S)])
+        q = w.q_decode(step)
+        got = fused.decode_step(k, v, q, SCALE)
+        split.append([k[s:s + 1] for s in range(S)], [v[s:s + 1] for s in range(S)])
+        ref_split = split.decode(q, SCALE)
+        for s in range(S):
+            orcs[s].append(k[s:s + 1], v[s:s + 1])
+        ref = oracle.attention_all(orcs, w.num_q_heads, q, w.dtype, np.arange(S + 1), SCALE, False, threads=8)
+        check_attention(got, ref, w.dtype, label=f"{w.name} fused step {step}")
+        check_attention(ref_split, ref, w.dtype, label=f"{w.name} separate calls step {step}")
+        if step % check_every == 0 or step == steps - 1:
+            pf, ps = fused.pool_view(), split.pool_view()
+            for s in range(S):
+                for h in range(w.num_kv_heads):
+                    st = pf.seq_state(fused.bt_np[s], s, int(pos[s]) + 1, h)
+                    compare_seq_state(st, orcs[s], h, label=f"fused step {step} seq {s} head {h}")
+                    st2 = ps.seq_state(split.bt_np[s], s, int(pos[s]) + 1, h)
+                    for key in ("k_code", "v_code", "k_s", "k_z", "v_s", "v_z", "k_res", "v_res"):
+                        assert np.array_equal(st[key], st2[key]), (step, s, h, key)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_fused_step_ragged_flushes(bits):
+    """Ragged lengths around the residual and group edges; 40 steps cross Key
+    flushes (R = 32) and Value quads, including a sequence that starts empty."""
+    w = inputs.config(1, bits=bits, k_group=32, v_group=32, residual=32, num_kv_heads=2, num_q_heads=8,
+                      num_seqs=6, seq_lens=[0, 1, 31, 32, 95, 300], extra_tokens=40, shuffle=True,
+                      pool_factor=1.5, n_outlier=2)
+    _run(w, 40)
+
+
+def test_fused_step_llama_shape_bf16():
+    w = inputs.config(5, num_seqs=3, seq_lens=[126, 255, 700], extra_tokens=6, shuffle=True, pool_factor=1.3)
+    _run(w, 6)
+
+
+def test_fused_step_with_splits():
+    """Few long sequences: the attention is split across work groups (merge
+    kernel); only split 0 appends and reads the touched tail."""
+    w = inputs.config(3, num_seqs=2, seq_lens=[5000, 8191], extra_tokens=4, shuffle=True, pool_factor=1.25)
+    _run(w, 4, check_every=3)
