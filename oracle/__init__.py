@@ -75,6 +75,9 @@ def lib():
             L.orc_attention.argtypes = [P, c.c_int, c.c_int, P, c.c_int, P, c.c_double, c.c_int,
                                         P, P, c.c_long, P, c.c_int]
             L.orc_attention.restype = c.c_int
+            L.orc_attention_raw_chunk.argtypes = [P, c.c_int, c.c_int, P, c.c_int, P, P, P, c.c_double,
+                                                  c.c_int, P, P, c.c_long, P, c.c_int]
+            L.orc_attention_raw_chunk.restype = c.c_int
             L.orc_hardware_threads.restype = c.c_int
             _lib = L
     return _lib
@@ -244,3 +247,37 @@ def attention_all(caches, H_Q, q_bits, q_dtype, cu_q, sigma, causal, threads=1) 
     heads = np.tile(np.arange(H_Q, dtype=np.int32), total)
     out = attention(caches, H_Q, q_bits, q_dtype, cu_q, sigma, causal, rows, heads, threads)
     return out.reshape(total, H_Q, caches[0].d)
+
+
+def attention_raw_chunk(caches, H_Q: int, q_bits: np.ndarray, q_dtype: int, cu_q, k_bits: np.ndarray,
+                        v_bits: np.ndarray, sigma: float, causal: bool, rows=None, heads=None,
+                        threads: int = 1) -> np.ndarray:
+    """Prefill outputs when each chunk's own Keys and Values take part at full
+    precision: caches hold each request's tokens BEFORE its chunk (P_s), the
+    chunk's rows k_bits / v_bits ([total_q][H][d] raw bits, indexed like q)
+    follow them, and row i of request s sits at position P_s + i.
+    rows / heads select items ([n][d] float64); None means every (row, head),
+    returned as [total_q][H_Q][d]."""
+    S = len(caches)
+    total = int(cu_q[-1])
+    full = rows is None
+    if full:
+        rows = np.repeat(np.arange(total, dtype=np.int32), H_Q)
+        heads = np.tile(np.arange(H_Q, dtype=np.int32), total)
+    arr = (ctypes.c_void_p * S)(*[c.handle for c in caches])
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    heads = np.ascontiguousarray(heads, dtype=np.int32)
+    H, d = caches[0].H, caches[0].d
+    assert rows.shape == heads.shape and cu.shape == (S + 1,)
+    assert k.shape == (total, H, d) and v.shape == (total, H, d)
+    out = np.zeros((rows.size, d), dtype=np.float64)
+    rc = lib().orc_attention_raw_chunk(ctypes.cast(arr, ctypes.c_void_p), S, H_Q, _ptr(q), q_dtype, _ptr(cu),
+                                       _ptr(k), _ptr(v), float(sigma), 1 if causal else 0, _ptr(rows),
+                                       _ptr(heads), rows.size, _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad attention arguments")
+    return out.reshape(total, H_Q, d) if full else out

@@ -254,26 +254,56 @@ struct SeqCache {
 // GQA: query head hq reads KV head hq / (H_Q / H_KV).
 // ---------------------------------------------------------------------------
 
-void attend_row(const SeqCache& c, const float* q, int hq, int H_Q, int pos,
-                double sigma, double* out) {
-    int g = H_Q / c.H;
-    int h = hq / g;
-    int n = pos + 1;
+// Softmax attention of one query over n tokens whose Keys and Values come
+// from kf(t, ch) and vf(t, ch).
+template <class KF, class VF>
+void attend_tokens(int d, const float* q, int n, KF kf, VF vf, double sigma, double* out) {
     std::vector<double> score(n);
     double m = -INFINITY;
     for (int t = 0; t < n; ++t) {
         double s = 0.0;
-        for (int ch = 0; ch < c.d; ++ch) s += (double)q[ch] * (double)c.k_tilde(h, t, ch);
+        for (int ch = 0; ch < d; ++ch) s += (double)q[ch] * (double)kf(t, ch);
         s *= sigma;
         score[t] = s;
         if (s > m) m = s;
     }
     double l = 0.0;
     for (int t = 0; t < n; ++t) { score[t] = std::exp(score[t] - m); l += score[t]; }
-    for (int ch = 0; ch < c.d; ++ch) out[ch] = 0.0;
+    for (int ch = 0; ch < d; ++ch) out[ch] = 0.0;
     for (int t = 0; t < n; ++t)
-        for (int ch = 0; ch < c.d; ++ch) out[ch] += score[t] * (double)c.v_tilde(h, t, ch);
-    for (int ch = 0; ch < c.d; ++ch) out[ch] /= l;
+        for (int ch = 0; ch < d; ++ch) out[ch] += score[t] * (double)vf(t, ch);
+    for (int ch = 0; ch < d; ++ch) out[ch] /= l;
+}
+
+void attend_row(const SeqCache& c, const float* q, int hq, int H_Q, int pos,
+                double sigma, double* out) {
+    int h = hq / (H_Q / c.H);
+    attend_tokens(c.d, q, pos + 1, [&](int t, int ch) { return c.k_tilde(h, t, ch); },
+                  [&](int t, int ch) { return c.v_tilde(h, t, ch); }, sigma, out);
+}
+
+// Prefill reading in which a chunk is quantised for storage only: the query
+// rows of a chunk see the reconstructed history the cache held before the
+// chunk (positions 0..P-1, quantised codes plus the residual of section 3.2)
+// and the chunk's own Keys and Values as given, at full precision (the
+// residual's rule that the newest tokens keep their precision, applied to the
+// whole chunk). kc, vc point at chunk row 0 of this request, rows of H*d
+// elements; the row sits at position P + i and sees n_chunk chunk tokens.
+void attend_row_raw_chunk(const SeqCache& c, const float* q, int hq, int H_Q, int n_chunk,
+                          const uint16_t* kc, const uint16_t* vc, double sigma, double* out) {
+    int h = hq / (H_Q / c.H);
+    int P = c.T;
+    size_t row = (size_t)c.H * c.d;
+    attend_tokens(c.d, q, P + n_chunk,
+                  [&](int t, int ch) {
+                      return t < P ? c.k_tilde(h, t, ch)
+                                   : load_elem(kc[(size_t)(t - P) * row + (size_t)h * c.d + ch], c.dtype);
+                  },
+                  [&](int t, int ch) {
+                      return t < P ? c.v_tilde(h, t, ch)
+                                   : load_elem(vc[(size_t)(t - P) * row + (size_t)h * c.d + ch], c.dtype);
+                  },
+                  sigma, out);
 }
 
 }  // namespace
@@ -383,6 +413,49 @@ int orc_attention(void** caches, int S, int H_Q, const uint16_t* q, int q_dtype,
                 qf[ch] = load_elem(q[((size_t)r * H_Q + hq) * d + ch], q_dtype);
             if (pos < 0) { for (int ch = 0; ch < d; ++ch) out[it * d + ch] = 0.0; continue; }
             attend_row(*c, qf.data(), hq, H_Q, pos, sigma, &out[it * d]);
+        }
+    };
+    int nt = threads > 0 ? threads : 1;
+    std::vector<std::thread> pool;
+    for (int i = 1; i < nt; ++i) pool.emplace_back(work);
+    work();
+    for (auto& th : pool) th.join();
+    return 0;
+}
+
+// Attention of chunks whose own tokens take part at full precision (see
+// attend_row_raw_chunk). caches[s] hold each request's tokens before its
+// chunk (P_s = their length); k_chunk, v_chunk: [total_q][H][d] raw bits in
+// the caches' dtype, indexed like q. Row i of request s sits at position
+// P_s + i and sees 0..P_s + i (causal) or 0..P_s + n_q,s - 1.
+int orc_attention_raw_chunk(void** caches, int S, int H_Q, const uint16_t* q, int q_dtype, const int* cu_q,
+                            const uint16_t* k_chunk, const uint16_t* v_chunk, double sigma, int causal,
+                            const int* rows, const int* heads, long n_items, double* out, int threads) {
+    if (S <= 0 || n_items < 0) return -1;
+    const SeqCache* c0 = static_cast<const SeqCache*>(caches[0]);
+    int d = c0->d, H = c0->H;
+    for (int s = 0; s < S; ++s) {
+        const SeqCache* c = static_cast<const SeqCache*>(caches[s]);
+        if (c->d != d || c->H != H || H_Q % c->H) return -1;
+    }
+    std::atomic<long> next(0);
+    auto work = [&]() {
+        std::vector<float> qf(d);
+        for (;;) {
+            long it = next.fetch_add(1);
+            if (it >= n_items) break;
+            int r = rows[it], hq = heads[it];
+            int s = 0;
+            while (s + 1 <= S && cu_q[s + 1] <= r) ++s;
+            const SeqCache* c = static_cast<const SeqCache*>(caches[s]);
+            int nq = cu_q[s + 1] - cu_q[s];
+            int i = r - cu_q[s];
+            int n_chunk = causal ? i + 1 : nq;
+            for (int ch = 0; ch < d; ++ch)
+                qf[ch] = load_elem(q[((size_t)r * H_Q + hq) * d + ch], q_dtype);
+            size_t base = (size_t)cu_q[s] * H * d;
+            attend_row_raw_chunk(*c, qf.data(), hq, H_Q, n_chunk, k_chunk + base, v_chunk + base, sigma,
+                                 &out[it * d]);
         }
     };
     int nt = threads > 0 ? threads : 1;

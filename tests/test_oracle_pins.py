@@ -422,3 +422,108 @@ def test_empty_sequence_row_is_zero():
     q = np.zeros((1, 1, 8), dtype=np.uint16)
     out = oracle.attention_all([c], 1, q, DT_F16, [0, 1], 1.0, False)
     assert np.all(out == 0)
+
+
+# ---------------------------------------------------------------------------
+# prefill with the chunk at full precision (the chunk is quantised for storage
+# only; its rows see the history as stored before the chunk plus the chunk's
+# own Keys and Values as given)
+# ---------------------------------------------------------------------------
+
+def _f64(bits):
+    return bits.view(np.float16).astype(np.float64)
+
+
+def test_raw_chunk_history_in_residual_equals_textbook():
+    """History shorter than R is all full precision, so every row is plain softmax attention
+    over the input stream, although the chunk (20 rows, R = 16) is long enough that storing
+    it first would quantise some of its own tokens."""
+    rng = np.random.default_rng(21)
+    H, HQ, d, G, Gv, R, P, nq = 2, 4, 16, 8, 8, 16, 10, 20
+    kb, vb = _stream(rng, P + nq, H, d)
+    c = oracle.SeqCache(H, d, 4, G, Gv, R, DT_F16, P + nq)
+    c.append(kb[:P], vb[:P])
+    qb = f16(rng.standard_normal((nq, HQ, d))).view(np.uint16)
+    sigma = 1 / math.sqrt(d)
+    cu = [0, nq]
+    out = oracle.attention_raw_chunk([c], HQ, qb, DT_F16, cu, kb[P:], vb[P:], sigma, True)
+    K, V = _f64(kb), _f64(vb)
+    for i in range(nq):
+        for hq in range(HQ):
+            want = _numpy_attention(_f64(qb)[i, hq], K[:P + i + 1, hq // 2], V[:P + i + 1, hq // 2], sigma)
+            np.testing.assert_allclose(out[i, hq], want, rtol=1e-12, atol=1e-13)
+    # the stored reading of the same chunk differs (its oldest chunk tokens were quantised)
+    c.append(kb[P:], vb[P:])
+    assert c.state()[1] > P
+    stored = oracle.attention_all([c], HQ, qb, DT_F16, cu, sigma, True)
+    assert not np.allclose(stored[-1], out[-1], rtol=1e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_raw_chunk_grid_exact_history_equals_textbook(bits):
+    """Quantised history that reproduces its inputs exactly, followed by a chunk of arbitrary
+    values: causal and non-causal rows equal softmax attention over the input stream."""
+    rng = np.random.default_rng(22)
+    H, HQ, d, G, Gv, R, P, nq = 2, 4, 16, 4, 8, 8, 37, 9
+    kh, vh = _grid_exact_stream(rng, P, H, d, G, Gv, bits)
+    kc, vc = _stream(rng, nq, H, d)
+    c = oracle.SeqCache(H, d, bits, G, Gv, R, DT_F16, P)
+    c.append(kh, vh)
+    assert c.state() == (37, 32, 29)
+    K, V = _f64(np.concatenate([kh, kc])), _f64(np.concatenate([vh, vc]))
+    qb = f16(rng.standard_normal((nq, HQ, d))).view(np.uint16)
+    for causal in (True, False):
+        out = oracle.attention_raw_chunk([c], HQ, qb, DT_F16, [0, nq], kc, vc, 0.3, causal)
+        for i in range(nq):
+            n = P + i + 1 if causal else P + nq
+            for hq in range(HQ):
+                want = _numpy_attention(_f64(qb)[i, hq], K[:n, hq // 2], V[:n, hq // 2], 0.3)
+                np.testing.assert_allclose(out[i, hq], want, rtol=1e-12, atol=1e-13)
+
+
+def test_raw_chunk_brute_force_ragged():
+    """Three requests with ragged history and chunk lengths (one with no history) and GQA 2:
+    every row equals numpy softmax over the reconstructed history followed by the raw chunk,
+    and selected items equal the corresponding full outputs."""
+    rng = np.random.default_rng(23)
+    H, HQ, d, G, Gv, R = 2, 4, 8, 4, 4, 4
+    hist, nq = [11, 0, 6], [3, 5, 1]
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    caches, Ks, Vs, kcs, vcs = [], [], [], [], []
+    for P, n in zip(hist, nq):
+        kb, vb = _stream(rng, P + n, H, d, kscale=np.where(np.arange(d) == 3, 20.0, 1.0))
+        c = oracle.SeqCache(H, d, 2, G, Gv, R, DT_F16, P + n)
+        c.append(kb[:P], vb[:P])
+        caches.append(c)
+        rec = [c.reconstruct(h) for h in range(H)]
+        Ks.append([np.concatenate([r[0], _f64(kb[P:, h])]) for h, r in enumerate(rec)])
+        Vs.append([np.concatenate([r[1], _f64(vb[P:, h])]) for h, r in enumerate(rec)])
+        kcs.append(kb[P:])
+        vcs.append(vb[P:])
+    kc, vc = np.concatenate(kcs), np.concatenate(vcs)
+    qb = f16(rng.standard_normal((cu[-1], HQ, d))).view(np.uint16)
+    sigma = 1 / math.sqrt(d)
+    out = oracle.attention_raw_chunk(caches, HQ, qb, DT_F16, cu, kc, vc, sigma, True)
+    for s in range(3):
+        for i in range(nq[s]):
+            n = hist[s] + i + 1
+            for hq in range(HQ):
+                want = _numpy_attention(_f64(qb)[cu[s] + i, hq], Ks[s][hq // 2][:n], Vs[s][hq // 2][:n], sigma)
+                np.testing.assert_allclose(out[cu[s] + i, hq], want, rtol=1e-12, atol=1e-13)
+    rows = np.array([8, 0, 3, 3], np.int32)
+    heads = np.array([1, 3, 0, 2], np.int32)
+    sel = oracle.attention_raw_chunk(caches, HQ, qb, DT_F16, cu, kc, vc, sigma, True, rows, heads)
+    assert np.array_equal(sel, out[rows, heads])
+
+
+def test_raw_chunk_single_token_without_history_is_its_value():
+    """One chunk token and no history: the softmax has one term, the output is that token's
+    Value for every query head."""
+    rng = np.random.default_rng(24)
+    H, HQ, d = 2, 6, 16
+    c = oracle.SeqCache(H, d, 4, 4, 4, 4, DT_F16, 1)
+    kb, vb = _stream(rng, 1, H, d)
+    qb = f16(rng.standard_normal((1, HQ, d))).view(np.uint16)
+    out = oracle.attention_raw_chunk([c], HQ, qb, DT_F16, [0, 1], kb, vb, 0.7, False)
+    for hq in range(HQ):
+        assert np.array_equal(out[0, hq], _f64(vb)[0, hq // 3])
