@@ -261,6 +261,33 @@ kivi_status kivi_prefill_attention(const kivi_cache* cache, int32_t num_seqs, in
                                    int32_t bt_stride, float softmax_scale, int32_t causal,
                                    void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* Chunked prefill in which the chunk is quantised for storage only: its rows
+ * attend over the history as the cache holds it (section 2 of "4.4 KV Cache
+ * 量化" over the quantised tokens plus the section 3.2 residual) followed by
+ * the chunk's own Keys and Values exactly as given (the pages leave the
+ * prefill open; this is the reading in which the newest tokens, here the
+ * whole chunk, keep full precision). Call it BEFORE kivi_append_tokens stores
+ * the same chunk, on the same stream: the append may quantise and overwrite
+ * the residual this call reads.
+ *   d_seq_lens_before[S]  tokens in the cache before the chunk; row i of
+ *                         sequence s sits at position seq_len_before_s + i
+ *   d_k_new, d_v_new      [total_q][H_KV][128] kv_dtype, the chunk's rows
+ *                         indexed like d_q (the arrays kivi_append_tokens
+ *                         then takes with d_cu_new = d_cu_q); 16-byte aligned
+ *   causal                1: row i sees positions 0..its own; 0: the whole
+ *                         history and chunk
+ *   d_block_table         pages must exist for positions < seq_len_before
+ *                         (the chunk's pages are not read)
+ * Other arguments as kivi_prefill_attention; the workspace is unused.
+ * Errors: INVALID_ARG, UNSUPPORTED, DEVICE.                                  */
+kivi_status kivi_prefill_attention_raw_chunk(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                             const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                             const int32_t* d_slot_ids, const int32_t* d_seq_lens_before,
+                                             const void* d_k_new, const void* d_v_new, int32_t max_seq_len,
+                                             const int32_t* d_block_table, int32_t bt_stride,
+                                             float softmax_scale, int32_t causal, void* d_out, void* d_ws,
+                                             size_t ws_bytes, void* stream);
+
 /* Message for the last failure on the calling thread ("" if none).           */
 const char* kivi_last_error(void);
 

@@ -157,6 +157,57 @@ DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int m
 
 }  // namespace kivi
 
+namespace {
+
+kivi_status check_heads(const kivi_cache* cache, int32_t num_q_heads) {
+    const int H = cache->cfg.num_kv_heads;
+    if (num_q_heads < 1) return fail(KIVI_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
+    if (num_q_heads % H)
+        return fail(KIVI_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, H);
+    if (num_q_heads / H > kivi::kMaxGqa)
+        return fail(KIVI_ERR_UNSUPPORTED, "%d query heads per KV head (at most %d)",
+                    num_q_heads / H, kivi::kMaxGqa);
+    return KIVI_OK;
+}
+
+kivi_status prefill_common(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads, const void* d_q,
+                           const int32_t* d_cu_q, int32_t max_q_len, const int32_t* d_slot_ids,
+                           const int32_t* d_seq_lens, int32_t max_seq_len, const void* d_k_chunk,
+                           const void* d_v_chunk, const int32_t* d_block_table, int32_t bt_stride,
+                           float softmax_scale, int32_t causal, void* d_out, void* stream, bool raw_chunk) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0)
+        return fail(KIVI_ERR_INVALID_ARG, "bad sizes");
+    if (causal != 0 && causal != 1) return fail(KIVI_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (num_seqs == 0 || max_q_len == 0) return ok();
+    if (!d_q || !d_cu_q || !d_slot_ids || !d_seq_lens || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (raw_chunk && (!d_k_chunk || !d_v_chunk))
+        return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (raw_chunk && (!aligned(d_k_chunk, 16) || !aligned(d_v_chunk, 16)))
+        return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+    if (!aligned(d_cu_q, 4) || !aligned(d_slot_ids, 4) || !aligned(d_seq_lens, 4) ||
+        !aligned(d_block_table, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    int err = kivi::launch_prefill(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_cu_q, max_q_len,
+                                   d_slot_ids, d_seq_lens, max_seq_len, raw_chunk ? d_k_chunk : nullptr,
+                                   raw_chunk ? d_v_chunk : nullptr, d_block_table, bt_stride, softmax_scale,
+                                   causal, d_out, stream);
+    return device_status(err, "prefill launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kivi_last_error(void) { return g_last_error.c_str(); }
@@ -274,18 +325,6 @@ kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seq
     return ok();
 }
 
-static kivi_status check_heads(const kivi_cache* cache, int32_t num_q_heads) {
-    const int H = cache->cfg.num_kv_heads;
-    if (num_q_heads < 1) return fail(KIVI_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
-    if (num_q_heads % H)
-        return fail(KIVI_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
-                    num_q_heads, H);
-    if (num_q_heads / H > kivi::kMaxGqa)
-        return fail(KIVI_ERR_UNSUPPORTED, "%d query heads per KV head (at most %d)",
-                    num_q_heads / H, kivi::kMaxGqa);
-    return KIVI_OK;
-}
-
 kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                   const void* d_q, const int32_t* d_slot_ids,
                                   const int32_t* d_seq_lens, int32_t max_seq_len,
@@ -373,29 +412,23 @@ kivi_status kivi_prefill_attention(const kivi_cache* cache, int32_t num_seqs, in
                                    void* d_out, void* d_ws, size_t ws_bytes, void* stream) {
     (void)d_ws;
     (void)ws_bytes;
-    kivi_status s = check_cache(cache);
-    if (s != KIVI_OK) return s;
-    s = check_heads(cache, num_q_heads);
-    if (s != KIVI_OK) return s;
-    if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0)
-        return fail(KIVI_ERR_INVALID_ARG, "bad sizes");
-    if (causal != 0 && causal != 1) return fail(KIVI_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (num_seqs == 0 || max_q_len == 0) return ok();
-    if (!d_q || !d_cu_q || !d_slot_ids || !d_seq_lens || !d_block_table || !d_out)
-        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
-    if (!aligned(d_q, 16) || !aligned(d_out, 16))
-        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
-    if (!aligned(d_cu_q, 4) || !aligned(d_slot_ids, 4) || !aligned(d_seq_lens, 4) ||
-        !aligned(d_block_table, 4))
-        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
-    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
-    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
-        softmax_scale == -std::numeric_limits<float>::infinity())
-        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
-    int err = kivi::launch_prefill(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_cu_q,
-                                   max_q_len, d_slot_ids, d_seq_lens, max_seq_len, d_block_table,
-                                   bt_stride, softmax_scale, causal, d_out, stream);
-    return device_status(err, "prefill launch");
+    return prefill_common(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_len, d_slot_ids, d_seq_lens,
+                          max_seq_len, nullptr, nullptr, d_block_table, bt_stride, softmax_scale, causal,
+                          d_out, stream, false);
+}
+
+kivi_status kivi_prefill_attention_raw_chunk(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                             const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                             const int32_t* d_slot_ids, const int32_t* d_seq_lens_before,
+                                             const void* d_k_new, const void* d_v_new, int32_t max_seq_len,
+                                             const int32_t* d_block_table, int32_t bt_stride,
+                                             float softmax_scale, int32_t causal, void* d_out, void* d_ws,
+                                             size_t ws_bytes, void* stream) {
+    (void)d_ws;
+    (void)ws_bytes;
+    return prefill_common(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_len, d_slot_ids, d_seq_lens_before,
+                          max_seq_len, d_k_new, d_v_new, d_block_table, bt_stride, softmax_scale, causal,
+                          d_out, stream, true);
 }
 
 }  // extern "C"

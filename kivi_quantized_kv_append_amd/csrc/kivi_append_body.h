@@ -375,7 +375,7 @@ __device__ __forceinline__ void append_token_value_wave(const AppendArgs& a, int
     if (!t.ok) return;
     const CacheView& V = *t.V;
     const int T0 = t.T0, T1 = T0 + 1, R = t.R;
-    const int TK0 = R * (T0 / R), TK1 = R * (T1 / R);
+    const int TK1 = R * (T1 / R);
     const int TV0 = max(0, T0 - R), TV1 = max(0, T1 - R);
     const int slot_new = T0 % R;
     const uint32_t kv = *reinterpret_cast<const uint32_t*>(t.inK + 2 * lane);

@@ -75,7 +75,8 @@ int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void*
 
 int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                    const int32_t* cu_q, int max_q_len, const int32_t* slot_ids,
-                   const int32_t* seq_lens, int max_seq_len, const int32_t* block_table,
-                   int bt_stride, float softmax_scale, int causal, void* out, void* stream);
+                   const int32_t* seq_lens, int max_seq_len, const void* k_chunk,
+                   const void* v_chunk, const int32_t* block_table, int bt_stride,
+                   float softmax_scale, int causal, void* out, void* stream);
 
 }  // namespace kivi

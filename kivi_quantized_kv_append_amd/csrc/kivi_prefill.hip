@@ -13,6 +13,12 @@
 // touch the residual. Causal rows see tokens 0 .. their own position; the
 // mask is applied per row only on tiles past the smallest row position.
 // Work groups hold 4 independent waves; each wave writes its rows' output.
+//
+// Second reading of the prefill (the pages leave it open): with a chunk given
+// at full precision, the call comes before the chunk is stored; seq_lens are
+// the lengths P before it, the chunk's rows sit at positions P .. P + n_q - 1,
+// and their Keys and Values are read from the chunk's own input rows instead
+// of the cache, so only the history is dequantised.
 
 #include <algorithm>
 
@@ -33,6 +39,8 @@ constexpr bool kFoldK = true;
 struct PrefillArgs {
     CacheView v;
     const uint16_t* q;
+    const uint16_t* k_chunk;  // chunk rows at full precision, or null
+    const uint16_t* v_chunk;
     const int32_t* cu_q;
     const int32_t* slot_ids;
     const int32_t* seq_lens;
@@ -76,12 +84,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     // ---- the sequence and this wave's rows ----
     const int q0 = a.cu_q[s];
     const int nq = a.cu_q[s + 1] - q0;
-    int T = a.seq_lens[s];
+    // P tokens come from the cache; with a full-precision chunk its nq tokens follow them
+    int P = a.seq_lens[s];
     const int slot = a.slot_ids[s];
-    if (slot < 0 || slot >= V.max_seqs || T < 0) T = 0;
+    const bool bad = slot < 0 || slot >= V.max_seqs || P < 0;
+    if (bad) P = 0;
+    const bool raw_chunk = a.k_chunk != nullptr;
+    const int T = bad ? 0 : P + (raw_chunk ? nq : 0);  // tokens the rows attend over
     const int row0 = (wg * kPWaves + wave) * kRowsPerWave;
     if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave
-    const int TK = V.R * (T / V.R), TV = max(0, T - V.R);
+    const int TK = V.R * (P / V.R), TV = max(0, P - V.R);
     const int n_main = TV / kTile;
     const int tk_tiles = TK / kTile;
     const int R = V.R;
@@ -290,12 +302,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int tb0 = (t >> a.tpg_shift) << a.tpg_shift;
         const int tpage = page_of(tb0 + lane);
         const int blk = valid_pg(__builtin_amdgcn_readlane(tpage, t - tb0));
-        if (blk < 0) continue;
+        const int p0 = t * kTile, pq = p0 + 4 * j;
+        if (blk < 0 && (t < tk_tiles || p0 < TV)) continue;  // codes without a page
         const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)h;
         const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
         const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
         const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
-        const int p0 = t * kTile, pq = p0 + 4 * j;
         f4 raw;
         if (t < tk_tiles) {
             uint32_t kw[BITS];
@@ -316,9 +328,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
             const uint8_t* qrow = reinterpret_cast<const uint8_t*>(lq + n * kQRow);
             const int pk = min(p0 + n, T - 1);  // A row: token n of the tile
+            const uint16_t* krow = pk < P ? ringK + (size_t)(pk % R) * kHeadDim
+                                          : a.k_chunk + ((size_t)(q0 + pk - P) * H + h) * kHeadDim;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 kr = *reinterpret_cast<const uint4*>(ringK + (size_t)(pk % R) * kHeadDim + 32 * i + 8 * j);
+                const uint4 kr = *reinterpret_cast<const uint4*>(krow + 32 * i + 8 * j);
                 const uint32_t ws[4] = {kr.x, kr.y, kr.z, kr.w};
                 h8 A;
 #pragma unroll
@@ -351,6 +365,26 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
             vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
+        if (raw_chunk && p0 + kTile > P) {  // chunk tokens replace their ring halves (uniform test)
+            bool inc[4];
+            const uint16_t* vrow[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                inc[r] = pq + r >= P && pq + r < T;
+                vrow[r] = a.v_chunk + ((size_t)(q0 + (inc[r] ? pq + r - P : 0)) * H + h) * kHeadDim + n;
+            }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                uint32_t w[2] = {vr[tt].x, vr[tt].y};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (inc[r]) {
+                        const uint32_t sh16 = 16u * (uint32_t)(r & 1);
+                        w[r >> 1] = (w[r >> 1] & ~(0xFFFFu << sh16)) | ((uint32_t)vrow[r][16 * tt] << sh16);
+                    }
+                vr[tt] = make_uint2(w[0], w[1]);
+            }
+        }
         float p[4], mx = -INFINITY;
         bool vis[4];
 #pragma unroll
@@ -372,7 +406,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int pr = pq + r;
-                const bool is_code = pr < TV, is_raw = !is_code && pr < T;
+                const bool is_code = pr < TV, is_raw = !is_code && pr < T;  // ring or chunk
                 const uint32_t mw = is_code ? vm[r * NG + gg] : 0u;
                 if (first_of_group) st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
                 const float code_v = (float)v_code_at<BITS>(vw, tt, r);
@@ -439,12 +473,14 @@ size_t prefill_lds_bytes() { return (size_t)kPWaves * prefill_wave_lds_bytes(); 
 
 int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void* q, const int32_t* cu_q,
                    int max_q_len, const int32_t* slot_ids, const int32_t* seq_lens, int max_seq_len,
-                   const int32_t* block_table, int bt_stride, float softmax_scale, int causal, void* out,
-                   void* stream) {
+                   const void* k_chunk, const void* v_chunk, const int32_t* block_table, int bt_stride,
+                   float softmax_scale, int causal, void* out, void* stream) {
     (void)max_seq_len;
     PrefillArgs a;
     a.v = v;
     a.q = static_cast<const uint16_t*>(q);
+    a.k_chunk = static_cast<const uint16_t*>(k_chunk);
+    a.v_chunk = static_cast<const uint16_t*>(v_chunk);
     a.cu_q = cu_q;
     a.slot_ids = slot_ids;
     a.seq_lens = seq_lens;

@@ -30,7 +30,8 @@ KIVI_BF16 = 1
 EXPORTED = [
     "kivi_cache_pool_bytes", "kivi_cache_capacity", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
     "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_step",
-    "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_last_error",
+    "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_prefill_attention_raw_chunk",
+    "kivi_last_error",
     "kivi_status_string",
 ]
 
@@ -83,6 +84,8 @@ def load():
         L.kivi_prefill_workspace_bytes.argtypes = [P, I32, I32, I32, I32, c.POINTER(S)]
         L.kivi_prefill_attention.argtypes = [P, I32, I32, P, P, I32, P, P, I32, P, I32, c.c_float,
                                              I32, P, P, S, P]
+        L.kivi_prefill_attention_raw_chunk.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, I32, P, I32,
+                                                       c.c_float, I32, P, P, S, P]
         L.kivi_last_error.argtypes = []
         L.kivi_last_error.restype = c.c_char_p
         L.kivi_status_string.argtypes = [c.c_int]
@@ -203,6 +206,17 @@ def kivi_prefill_attention(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_len,
                                          _ptr(d_block_table), bt_stride, float(softmax_scale),
                                          int(causal), _ptr(d_out), _ptr(d_ws), ws_bytes,
                                          _stream(stream)))
+
+
+def kivi_prefill_attention_raw_chunk(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_len, d_slot_ids,
+                                     d_seq_lens_before, d_k_new, d_v_new, max_seq_len, d_block_table, bt_stride,
+                                     softmax_scale, causal, d_out, d_ws=None, ws_bytes=0, stream=None):
+    _check(load().kivi_prefill_attention_raw_chunk(cache, num_seqs, num_q_heads, _ptr(d_q), _ptr(d_cu_q),
+                                                   max_q_len, _ptr(d_slot_ids), _ptr(d_seq_lens_before),
+                                                   _ptr(d_k_new), _ptr(d_v_new), max_seq_len,
+                                                   _ptr(d_block_table), bt_stride, float(softmax_scale),
+                                                   int(causal), _ptr(d_out), _ptr(d_ws), ws_bytes,
+                                                   _stream(stream)))
 
 
 def kivi_last_error() -> str:

@@ -372,6 +372,27 @@ class GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16)
 
+    def prefill_raw_chunk(self, q_bits: np.ndarray, cu_q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                          scale: float, causal=True, seqs=None):
+        """kivi_prefill_attention_raw_chunk over the cache as it stands (self.lens are the
+        lengths before the chunk); k_rows / v_rows [total_q][H][128] are the chunk's rows."""
+        torch = self.torch
+        seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)
+        HQ = self.w.num_q_heads
+        q = self.t(np.ascontiguousarray(q_bits).view(np.int16))
+        k = self.t(np.ascontiguousarray(k_rows).view(np.int16))
+        v = self.t(np.ascontiguousarray(v_rows).view(np.int16))
+        out = torch.zeros((q_bits.shape[0], HQ, D), dtype=torch.int16, device=self.device)
+        bt = self.t(self.bt_np[seqs])
+        mql = int(np.diff(cu_q).max())
+        msl = int((self.lens[seqs] + np.diff(cu_q)).max())
+        kivi.kivi_prefill_attention_raw_chunk(self.handle, len(seqs), HQ, q, self.t(cu_q.astype(np.int32)), mql,
+                                              self.t(np.asarray(seqs, np.int32)),
+                                              self.t(self.lens[seqs].astype(np.int32)), k, v, msl, bt,
+                                              bt.shape[1], scale, int(causal), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
     def pool_view(self) -> PoolView:
         self.torch.cuda.synchronize()
         return PoolView(self.pool.cpu().numpy(), self.layout, self.cfg_dict)

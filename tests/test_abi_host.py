@@ -177,6 +177,19 @@ def test_call_argument_checks_launch_nothing():
             kivi.kivi_prefill_attention(h, 2, 32, D, D, 16, D, D, 4096, D, 1, 0.1, 2, D)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
         assert "causal" in kivi.kivi_last_error()
+        # prefill with the chunk at full precision: the chunk's rows are required and aligned
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_prefill_attention_raw_chunk(h, 2, 32, D, D, 16, D, D, None, D, 4096, D, 1, 0.1, 1, D)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        assert "k_new" in kivi.kivi_last_error()
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_prefill_attention_raw_chunk(h, 2, 32, D, D, 16, D, D, D, D + 8, 4096, D, 1, 0.1, 1, D)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_prefill_attention_raw_chunk(h, 2, 30, D, D, 16, D, D, D, D, 4096, D, 1, 0.1, 1, D)
+        assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+        kivi.kivi_prefill_attention_raw_chunk(h, 0, 32, None, None, 0, None, None, None, None, 0, None, 1, 0.1, 1,
+                                              None)  # no sequences: a no-op
     finally:
         kivi.kivi_cache_destroy(h)
 
