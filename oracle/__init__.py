@@ -64,7 +64,7 @@ def lib():
             L.orc_dequant.argtypes = [c.c_int, c.c_uint16, c.c_uint16]
             L.orc_dequant.restype = c.c_float
             L.orc_dequant_array.argtypes = [P, P, P, P, c.c_long]
-            L.orc_cache_new.argtypes = [c.c_int] * 8
+            L.orc_cache_new.argtypes = [c.c_int] * 9
             L.orc_cache_new.restype = P
             L.orc_cache_free.argtypes = [P]
             L.orc_cache_append.argtypes = [P, c.c_int, P, P]
@@ -151,12 +151,16 @@ class SeqCache:
       k_s, k_z: [H][Tmax//G + 1][d] fp16 bits (group j covers tokens jG..jG+G-1)
       v_s, v_z: [H][Tmax][d//Gv] fp16 bits
       k_raw, v_raw: [H][Tmax][d] input bits (the residual is read from here)
+
+    v_flush=0 keeps the sliding Value window of the newest R tokens; v_flush=1 quantises
+    the Value tokens of the residual together with the Keys at every Key flush.
     """
 
-    def __init__(self, H, d, bits, G, Gv, R, dtype, Tmax):
+    def __init__(self, H, d, bits, G, Gv, R, dtype, Tmax, v_flush=0):
         self.H, self.d, self.bits, self.G, self.Gv, self.R, self.dtype, self.Tmax = \
             H, d, bits, G, Gv, R, dtype, Tmax
-        self._h = lib().orc_cache_new(H, d, bits, G, Gv, R, dtype, Tmax)
+        self.v_flush = v_flush
+        self._h = lib().orc_cache_new(H, d, bits, G, Gv, R, dtype, Tmax, v_flush)
         if not self._h:
             raise ValueError("oracle: unsupported cache parameters")
 

@@ -165,20 +165,27 @@ float dequant(uint8_t code, uint16_t s16, uint16_t z16) {
 // of Gv (section 3.1).
 // The raw stream of every appended token is kept; tokens at positions not yet
 // quantised are the residual.
+// Value flush variant (vflush = 1): section 3.2 fixes the sliding Value
+// window above and leaves open a cache that empties its Value residual when
+// the Key residual flushes. Read plainly: at every Key flush the same R tokens
+// also leave the Value residual, each still quantised per token over channel
+// groups of Gv (section 3.1), so Keys and Values share one boundary
+// TV = TK = R floor(T/R).
 // ---------------------------------------------------------------------------
 
 struct SeqCache {
     int H, d, bits, G, Gv, R, dtype, Tmax;
+    int vflush;   // 0: sliding Value window; 1: Values flush with the Keys
     int T = 0;    // tokens appended
     int TK = 0;   // Key tokens quantised (a multiple of R)
-    int TV = 0;   // Value tokens quantised (max(0, T - R))
+    int TV = 0;   // Value tokens quantised (max(0, T - R); TK when vflush)
     std::vector<uint16_t> k_raw, v_raw;  // [H][Tmax][d] input bits
     std::vector<uint8_t> k_code, v_code; // [H][Tmax][d] one code per element
     std::vector<uint16_t> k_s, k_z;      // [H][Tmax/G][d]
     std::vector<uint16_t> v_s, v_z;      // [H][Tmax][d/Gv]
 
-    SeqCache(int H_, int d_, int bits_, int G_, int Gv_, int R_, int dtype_, int Tmax_)
-        : H(H_), d(d_), bits(bits_), G(G_), Gv(Gv_), R(R_), dtype(dtype_), Tmax(Tmax_),
+    SeqCache(int H_, int d_, int bits_, int G_, int Gv_, int R_, int dtype_, int Tmax_, int vflush_)
+        : H(H_), d(d_), bits(bits_), G(G_), Gv(Gv_), R(R_), dtype(dtype_), Tmax(Tmax_), vflush(vflush_),
           k_raw((size_t)H_ * Tmax_ * d_), v_raw((size_t)H_ * Tmax_ * d_),
           k_code((size_t)H_ * Tmax_ * d_), v_code((size_t)H_ * Tmax_ * d_),
           k_s((size_t)H_ * (Tmax_ / G_ + 1) * d_), k_z((size_t)H_ * (Tmax_ / G_ + 1) * d_),
@@ -210,20 +217,27 @@ struct SeqCache {
     }
 
     // Append one token (all heads): k, v are [H][d] raw bits.
-    // Order: Value eviction of the token leaving the window, then the new
-    // token enters the residual, then the Key flush if the residual is full.
+    // Order: Value eviction of the token leaving the window (sliding window
+    // only), then the new token enters the residual, then the Key flush if
+    // the residual is full (with the vflush variant, the Value flush of the
+    // same R tokens).
     void append_one(const uint16_t* k, const uint16_t* v) {
         int t = T;
         for (int h = 0; h < H; ++h) {
-            if (t >= R) quantize_value_token(h, t - R);
+            if (!vflush && t >= R) quantize_value_token(h, t - R);
             std::memcpy(&k_raw[tok(h, t)], k + (size_t)h * d, d * sizeof(uint16_t));
             std::memcpy(&v_raw[tok(h, t)], v + (size_t)h * d, d * sizeof(uint16_t));
         }
-        if (t >= R) TV = t - R + 1;
+        if (!vflush && t >= R) TV = t - R + 1;
         if ((t + 1) % R == 0) {
             for (int h = 0; h < H; ++h)
                 for (int j = (t + 1 - R) / G; j < (t + 1) / G; ++j) quantize_key_group(h, j);
             TK = t + 1;
+            if (vflush) {
+                for (int h = 0; h < H; ++h)
+                    for (int p = t + 1 - R; p <= t; ++p) quantize_value_token(h, p);
+                TV = t + 1;
+            }
         }
         T = t + 1;
     }
@@ -339,11 +353,11 @@ void orc_dequant_array(const uint8_t* codes, const uint16_t* s16, const uint16_t
 }
 
 // --- sequence cache -----------------------------------------------------------
-void* orc_cache_new(int H, int d, int bits, int G, int Gv, int R, int dtype, int Tmax) {
+void* orc_cache_new(int H, int d, int bits, int G, int Gv, int R, int dtype, int Tmax, int vflush) {
     if (H <= 0 || d <= 0 || (bits != 2 && bits != 4) || G <= 0 || Gv <= 0 || d % Gv ||
-        R <= 0 || R % G || Tmax < 0 || (dtype != DT_F16 && dtype != DT_BF16))
+        R <= 0 || R % G || Tmax < 0 || (dtype != DT_F16 && dtype != DT_BF16) || (vflush != 0 && vflush != 1))
         return nullptr;
-    return new SeqCache(H, d, bits, G, Gv, R, dtype, Tmax);
+    return new SeqCache(H, d, bits, G, Gv, R, dtype, Tmax, vflush);
 }
 void orc_cache_free(void* p) { delete static_cast<SeqCache*>(p); }
 

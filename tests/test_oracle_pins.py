@@ -230,21 +230,23 @@ def _as_f32(bits, dtype):
 
 @pytest.mark.parametrize("bits,G,Gv,R", [(4, 4, 4, 4), (2, 4, 8, 8), (4, 8, 16, 16), (2, 32, 32, 64)])
 @pytest.mark.parametrize("dtype", [DT_F16, DT_BF16])
-def test_cache_state_is_direct_grouping_of_stream(bits, G, Gv, R, dtype):
-    """After T tokens: T_K = R floor(T/R), T_V = max(0, T-R); Key group j of channel c is
-    the quantisation of tokens jG..jG+G-1 of that channel alone; Value token t group g is
-    the quantisation of channels gGv..gGv+Gv-1 of that token alone."""
+@pytest.mark.parametrize("v_flush", [0, 1])
+def test_cache_state_is_direct_grouping_of_stream(bits, G, Gv, R, dtype, v_flush):
+    """After T tokens: T_K = R floor(T/R), T_V = max(0, T-R) (T_V = T_K when Values flush
+    with the Keys); Key group j of channel c is the quantisation of tokens jG..jG+G-1 of
+    that channel alone; Value token t group g is the quantisation of channels
+    gGv..gGv+Gv-1 of that token alone."""
     rng = np.random.default_rng(9)
     H, d, T = 2, 32, 3 * R + R // 2 + 1
     kb, vb = _stream(rng, T, H, d, dtype)
-    c = oracle.SeqCache(H, d, bits, G, Gv, R, dtype, T)
+    c = oracle.SeqCache(H, d, bits, G, Gv, R, dtype, T, v_flush=v_flush)
     t = 0
     while t < T:  # appends of random sizes
         n = int(min(T - t, rng.integers(1, 2 * R)))
         c.append(kb[t:t + n], vb[t:t + n])
         t += n
         Tn, TK, TV = c.state()
-        assert (Tn, TK, TV) == (t, R * (t // R), max(0, t - R))
+        assert (Tn, TK, TV) == (t, R * (t // R), R * (t // R) if v_flush else max(0, t - R))
     a = c.arrays()
     kf, vf = _as_f32(kb, dtype), _as_f32(vb, dtype)
     Tn, TK, TV = c.state()
@@ -262,6 +264,68 @@ def test_cache_state_is_direct_grouping_of_stream(bits, G, Gv, R, dtype):
         # residual keeps the input bits
         assert np.array_equal(a["k_raw"][h, TK:T], kb[TK:T, h])
         assert np.array_equal(a["v_raw"][h, TV:T], vb[TV:T, h])
+
+
+def _dequant_f32(codes, s16, z16):
+    """x = fl32(fl32(code * S) + Z), two single-precision roundings."""
+    S = np.asarray(s16, np.uint16).view(np.float16).astype(np.float32)
+    Z = np.asarray(z16, np.uint16).view(np.float16).astype(np.float32)
+    return (codes.astype(np.float32) * S).astype(np.float32) + Z
+
+
+def test_value_flush_variant_keeps_keys_and_early_values():
+    """Flushing Values with the Keys changes only when Value tokens leave the residual:
+    Key state is the same as with the sliding window, and every Value token both caches
+    have quantised carries the same codes and parameters (per-token quantisation does
+    not depend on when it runs)."""
+    rng = np.random.default_rng(21)
+    H, d, G, Gv, R, T = 2, 16, 4, 8, 8, 45
+    kb, vb = _stream(rng, T, H, d)
+    cw = oracle.SeqCache(H, d, 4, G, Gv, R, DT_F16, T)
+    cu = oracle.SeqCache(H, d, 4, G, Gv, R, DT_F16, T, v_flush=1)
+    for t in range(T):
+        cw.append(kb[t:t + 1], vb[t:t + 1])
+        cu.append(kb[t:t + 1], vb[t:t + 1])
+        _, TKw, TVw = cw.state()
+        _, TKu, TVu = cu.state()
+        assert TKw == TKu == TVu and TVw == max(0, t + 1 - R)
+    aw, au = cw.arrays(), cu.arrays()
+    _, TK, TVu = cu.state()
+    TVw = cw.state()[2]
+    for name in ("k_code", "k_s", "k_z", "k_raw"):
+        assert np.array_equal(aw[name], au[name]), name
+    for name in ("v_code", "v_s", "v_z"):
+        assert np.array_equal(aw[name][:, :TVw], au[name][:, :TVw]), name
+    assert TVu == 40 and TVw == 37  # tokens 37..39 are codes in one cache, residual in the other
+
+
+def test_value_flush_variant_attention_brute_force():
+    """Attention over a cache whose Values flush with the Keys, against numpy float64
+    softmax over K and V reconstructed by hand: codes of tokens below T_K = T_V restored
+    as code * S + Z, the R-floor(T/R) newest tokens at full precision."""
+    rng = np.random.default_rng(22)
+    H, HQ, d, G, Gv, R, T = 1, 2, 16, 4, 8, 8, 27
+    kb, vb = _stream(rng, T, H, d)
+    c = oracle.SeqCache(H, d, 4, G, Gv, R, DT_F16, T, v_flush=1)
+    c.append(kb, vb)
+    assert c.state() == (T, 24, 24)
+    kf, vf = _as_f32(kb, DT_F16)[:, 0], _as_f32(vb, DT_F16)[:, 0]
+    K, V = kf.copy(), vf.copy()
+    for j in range(24 // G):
+        for ch in range(d):
+            codes, s, z = oracle.quantize_group(kf[j * G:(j + 1) * G, ch], 4)
+            K[j * G:(j + 1) * G, ch] = _dequant_f32(codes, s, z)
+    for t in range(24):
+        for g in range(d // Gv):
+            codes, s, z = oracle.quantize_group(vf[t, g * Gv:(g + 1) * Gv], 4)
+            V[t, g * Gv:(g + 1) * Gv] = _dequant_f32(codes, s, z)
+    assert not np.array_equal(V[16:24], vf[16:24])  # the flushed tokens are restored codes
+    qb = f16(rng.standard_normal((1, HQ, d))).view(np.uint16)
+    q = qb.view(np.float16).astype(np.float64)
+    out = oracle.attention_all([c], HQ, qb, DT_F16, [0, 1], 0.25, False)
+    for hq in range(HQ):
+        want = _numpy_attention(q[0, hq], K, V, 0.25)
+        np.testing.assert_allclose(out[0, hq], want, rtol=1e-12, atol=1e-13)
 
 
 def test_key_outlier_channel_isolated():
