@@ -77,7 +77,16 @@ typedef enum kivi_dtype {
  *   num_blocks    physical pages in the pool (>= 1)
  *   max_seqs      residual slots (>= 1); a sequence uses the slot the caller
  *                 assigns it
- *   kv_dtype      kivi_dtype of the K/V tokens, the residual and q/out      */
+ *   kv_dtype      kivi_dtype of the K/V tokens, the residual and q/out
+ *   v_flush       when Value tokens leave the residual ("4.4 KV Cache 量化",
+ *                 section 3.2 gives the window; the other is its open
+ *                 variant): 0 = sliding window, the oldest of the R newest
+ *                 tokens is quantised as each new token arrives, so the
+ *                 Value boundary is max(0, T - R); 1 = with the Keys, the R
+ *                 residual tokens are quantised (each per token over Gv
+ *                 channels) at every Key flush, so the boundary is
+ *                 R*floor(T/R) for both. Any other value is
+ *                 KIVI_ERR_UNSUPPORTED. A zero-initialised config takes 0. */
 typedef struct kivi_cache_config {
     int32_t num_kv_heads;
     int32_t head_dim;
@@ -89,6 +98,7 @@ typedef struct kivi_cache_config {
     int32_t num_blocks;
     int32_t max_seqs;
     int32_t kv_dtype;
+    int32_t v_flush;
 } kivi_cache_config;
 
 /* Byte offsets of the sub-arrays inside the pool (each 256-byte aligned) and
@@ -227,7 +237,8 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
  * when the residual fills, the residual write; "4.4 KV Cache 量化", section
  * 3.2) and then attend with that token's query over the sequence's T + 1
  * tokens (as kivi_decode_attention). The cache state and the outputs are
- * those of the two calls in a row.
+ * those of the two calls in a row. A cache with v_flush = 1 (a flush step
+ * quantises R Value tokens) runs the step as those two launches.
  *   d_seq_lens_before[S]  tokens before this step (the query sits at position T)
  *   d_k_new, d_v_new      [S][H_KV][128] kv_dtype, row s is sequence s's token
  *   max_seq_len           host upper bound of d_seq_lens_before + 1 (also

@@ -73,6 +73,8 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     if (c.max_seqs < 1) return fail(KIVI_ERR_INVALID_ARG, "max_seqs %d < 1", c.max_seqs);
     if (c.kv_dtype != KIVI_F16 && c.kv_dtype != KIVI_BF16)
         return fail(KIVI_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c.kv_dtype);
+    if (c.v_flush != 0 && c.v_flush != 1)
+        return fail(KIVI_ERR_UNSUPPORTED, "v_flush %d unsupported (0 or 1)", c.v_flush);
 
     const uint64_t H = (uint64_t)c.num_kv_heads;
     kivi_layout L{};
@@ -129,6 +131,7 @@ CacheView view_of(const kivi_cache* c) {
     v.num_blocks = c->cfg.num_blocks;
     v.max_seqs = c->cfg.max_seqs;
     v.dtype = c->cfg.kv_dtype;
+    v.vflush = c->cfg.v_flush;
     v.code_bytes = (int)L.code_bytes;
     v.k_meta_bytes = (int)L.k_meta_bytes;
     v.v_meta_bytes = (int)L.v_meta_bytes;
@@ -386,9 +389,22 @@ kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0,
                     plan.ws_bytes);
     if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    int err = kivi::launch_decode_step(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_slot_ids,
-                                       d_seq_lens_before, d_k_new, d_v_new, d_block_table, bt_stride,
-                                       softmax_scale, d_out, static_cast<float*>(d_ws), plan, stream);
+    const kivi::CacheView view = kivi::view_of(cache);
+    if (view.vflush) {
+        // Values flush with the Keys: a flush step quantises R Value tokens,
+        // which the append kernel spreads over its work group; the attention
+        // follows on the same stream over the seq_lens_before + 1 tokens.
+        int err = kivi::launch_append(view, num_seqs, d_slot_ids, d_seq_lens_before, nullptr, 1, d_k_new,
+                                      d_v_new, d_block_table, bt_stride, stream);
+        if (err == 0)
+            err = kivi::launch_decode(view, num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_lens_before,
+                                      d_block_table, bt_stride, softmax_scale, d_out, static_cast<float*>(d_ws),
+                                      plan, stream, 1);
+        return device_status(err, "decode step launch");
+    }
+    int err = kivi::launch_decode_step(view, num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_lens_before, d_k_new,
+                                       d_v_new, d_block_table, bt_stride, softmax_scale, d_out,
+                                       static_cast<float*>(d_ws), plan, stream);
     return device_status(err, "decode step launch");
 }
 

@@ -16,8 +16,9 @@ template <int BITS, int DT>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     __shared__ AppendShared<kAppendThreads> sm;
     const int s = blockIdx.x / a.v.H, h = blockIdx.x % a.v.H;
-    const int row0 = a.cu_new[s];
-    const int n = a.cu_new[s + 1] - row0;
+    // no row offsets: one row per sequence, in sequence order
+    const int row0 = a.cu_new ? a.cu_new[s] : s;
+    const int n = a.cu_new ? a.cu_new[s + 1] - row0 : 1;
     append_body<BITS, DT, kAppendThreads>(a, s, h, row0, n, threadIdx.x, blockIdx.y, gridDim.y, sm);
 }
 

@@ -6,8 +6,9 @@
 // appends:
 //   * Key: tokens [R*floor(T0/R), R*floor(T1/R)) are quantised per channel,
 //     G tokens per group (the residual reached R tokens that many times);
-//   * Value: tokens [max(0,T0-R), max(0,T1-R)) left the R-token window and
-//     are quantised per token, Gv channels per group;
+//   * Value: tokens [TV(T0), TV(T1)) leave the residual and are quantised
+//     per token, Gv channels per group; TV(T) = max(0, T-R) for the sliding
+//     window, R*floor(T/R) when Values flush with the Keys;
 //   * the residual ring receives the new rows that stay full precision.
 // Phase A (all quantisation) reads the old ring and the new rows; a barrier
 // separates it from phase B (ring writes), which may overwrite ring slots
@@ -70,7 +71,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
     const int T1 = T0 + n;
     const int R = V.R, G = V.G, Gv = V.Gv, Bk = V.Bk;
     const int TK0 = R * (T0 / R), TK1 = R * (T1 / R);
-    const int TV0 = max(0, T0 - R), TV1 = max(0, T1 - R);
+    const int TV0 = value_boundary(V, T0), TV1 = value_boundary(V, T1);
     const int32_t* bt = a.block_table + (size_t)s * a.bt_stride;
     const int bt_len = a.bt_stride;
 
@@ -376,6 +377,8 @@ __device__ __forceinline__ void append_token_value_wave(const AppendArgs& a, int
     const CacheView& V = *t.V;
     const int T0 = t.T0, T1 = T0 + 1, R = t.R;
     const int TK1 = R * (T1 / R);
+    // sliding window only: a cache whose Values flush with the Keys never
+    // takes the fused step
     const int TV0 = max(0, T0 - R), TV1 = max(0, T1 - R);
     const int slot_new = T0 % R;
     const uint32_t kv = *reinterpret_cast<const uint32_t*>(t.inK + 2 * lane);

@@ -74,6 +74,9 @@ struct DecodeArgs {
     // split 0 of each (sequence, KV head) appends the token (rows of app.k_new
     // / app.v_new in sequence order) before it attends over T + 1 tokens.
     int fuse;
+    // Tokens appended by an earlier launch on the stream after seq_lens was
+    // taken (0 or 1): the sequence holds seq_lens[s] + len_add tokens.
+    int len_add;
     AppendArgs app;
 };
 
@@ -98,15 +101,16 @@ __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
     c.h = h;
     c.g = a.gqa;
     const int T_in = a.seq_lens[s];
-    int T = T_in + a.fuse;
+    int T = T_in + a.fuse + a.len_add;
     c.slot = a.slot_ids[s];
     if (c.slot < 0 || c.slot >= V.max_seqs || T_in < 0) T = 0;
     c.T = T;
     c.TK = V.R * (T / V.R);
-    c.TV = max(0, T - V.R);
+    c.TV = value_boundary(V, T);
     // main tiles: Key and Value both quantised before this call (a fused step
-    // writes only at or past the old Value boundary)
-    c.n_main = max(0, T - a.fuse - V.R) / kTile;
+    // writes only at or past the old Value boundary; both boundaries are
+    // multiples of 16 or past the Key one)
+    c.n_main = value_boundary(V, max(0, T - a.fuse)) / kTile;
     c.bt = a.block_table + (size_t)s * a.bt_stride;
     c.bt_len = a.bt_stride;
     return c;
@@ -704,9 +708,10 @@ int launch_decode_args(DecodeArgs& a, const CacheView& v, int num_seqs, int num_
 int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                   const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
                   int bt_stride, float softmax_scale, void* out, float* partials,
-                  const DecodePlan& plan, void* stream) {
+                  const DecodePlan& plan, void* stream, int len_add) {
     DecodeArgs a{};
     a.fuse = 0;
+    a.len_add = len_add;
     return launch_decode_args(a, v, num_seqs, num_q_heads, q, slot_ids, seq_lens, block_table, bt_stride,
                               softmax_scale, out, partials, plan, plan.lds_bytes, stream);
 }

@@ -4,6 +4,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <hip/hip_runtime.h>
+
 #include "kivi.h"
 
 struct kivi_cache {
@@ -28,7 +30,14 @@ struct CacheView {
     uint16_t* v_ring;
     int H, bits, G, Gv, R, Bk, num_blocks, max_seqs, dtype;
     int code_bytes, k_meta_bytes, v_meta_bytes, ring_elems;
+    int vflush;  // 0: sliding Value window; 1: Values flush with the Keys
 };
+
+// Value tokens quantised after T appends: the window keeps the R newest
+// tokens; with vflush the Values share the Key boundary R*floor(T/R).
+__host__ __device__ inline int value_boundary(const CacheView& v, int T) {
+    return v.vflush ? v.R * (T / v.R) : (T > v.R ? T - v.R : 0);
+}
 
 CacheView view_of(const kivi_cache* c);
 
@@ -68,10 +77,12 @@ int launch_decode_step(const CacheView& v, int num_seqs, int num_q_heads, const 
                        const void* v_new, const int32_t* block_table, int bt_stride, float softmax_scale,
                        void* out, float* partials, const DecodePlan& plan, void* stream);
 
+// len_add: tokens an earlier launch on the stream appended after seq_lens
+// was taken (0 or 1).
 int launch_decode(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                   const int32_t* slot_ids, const int32_t* seq_lens, const int32_t* block_table,
                   int bt_stride, float softmax_scale, void* out, float* partials,
-                  const DecodePlan& plan, void* stream);
+                  const DecodePlan& plan, void* stream, int len_add = 0);
 
 int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void* q,
                    const int32_t* cu_q, int max_q_len, const int32_t* slot_ids,

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int T = bad ? 0 : P + (raw_chunk ? nq : 0);  // tokens the rows attend over
     const int row0 = (wg * kPWaves + wave) * kRowsPerWave;
     if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave
-    const int TK = V.R * (P / V.R), TV = max(0, P - V.R);
+    const int TK = V.R * (P / V.R), TV = value_boundary(V, P);
     const int n_main = TV / kTile;
     const int tk_tiles = TK / kTile;
     const int R = V.R;

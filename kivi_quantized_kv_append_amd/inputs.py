@@ -68,6 +68,7 @@ class Workload:
     pool_factor: float
     seed: int = 0
     cfg_id: int = 0
+    v_flush: int = 0              # 1: Values leave the residual with the Keys
 
     # ---- pages ---------------------------------------------------------------
     @property

@@ -45,7 +45,7 @@ class KiviError(RuntimeError):
 class kivi_cache_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_kv_heads", "head_dim", "bits", "k_group", "v_group", "residual", "block_size",
-        "num_blocks", "max_seqs", "kv_dtype")]
+        "num_blocks", "max_seqs", "kv_dtype", "v_flush")]
 
 
 class kivi_layout(ctypes.Structure):
@@ -126,9 +126,9 @@ def _stream(s) -> int | None:
 
 
 def make_config(num_kv_heads, bits, k_group, v_group, residual, block_size, num_blocks, max_seqs,
-                kv_dtype=KIVI_F16, head_dim=128) -> kivi_cache_config:
+                kv_dtype=KIVI_F16, head_dim=128, v_flush=0) -> kivi_cache_config:
     return kivi_cache_config(num_kv_heads, head_dim, bits, k_group, v_group, residual, block_size,
-                             num_blocks, max_seqs, kv_dtype)
+                             num_blocks, max_seqs, kv_dtype, v_flush)
 
 
 def kivi_cache_pool_bytes(cfg: kivi_cache_config) -> int:

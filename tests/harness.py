@@ -93,7 +93,7 @@ class PoolView:
         c, L = self.c, self.L
         H, bits, G, Gv, R, Bk = c["H"], c["bits"], c["G"], c["Gv"], c["R"], c["Bk"]
         TK = R * (T // R)
-        TV = max(0, T - R)
+        TV = TK if c.get("v_flush", 0) else max(0, T - R)
         out = {"T": T, "TK": TK, "TV": TV}
         cb = L["code_bytes"]
 
@@ -271,10 +271,10 @@ class GpuCache:
         self.w = w
         self.device = device
         self.cfg_dict = {"H": w.num_kv_heads, "bits": w.bits, "G": w.k_group, "Gv": w.v_group,
-                         "R": w.residual, "Bk": w.block_size}
+                         "R": w.residual, "Bk": w.block_size, "v_flush": w.v_flush}
         nb = num_blocks or w.num_blocks
         self.cfg = kivi.make_config(w.num_kv_heads, w.bits, w.k_group, w.v_group, w.residual,
-                                    w.block_size, nb, w.num_seqs, w.dtype)
+                                    w.block_size, nb, w.num_seqs, w.dtype, v_flush=w.v_flush)
         self.nbytes = kivi.kivi_cache_pool_bytes(self.cfg)
         if fill_garbage:
             g = torch.Generator(device="cpu").manual_seed(123)
@@ -404,7 +404,7 @@ def oracle_caches(w: inputs.Workload, lens=None):
     out = []
     for s in range(w.num_seqs):
         c = oracle.SeqCache(w.num_kv_heads, D, w.bits, w.k_group, w.v_group, w.residual, w.dtype,
-                            int(w.final_lens[s]))
+                            int(w.final_lens[s]), v_flush=w.v_flush)
         k, v = w.kv_stream(s, 0, int(lens[s]))
         c.append(k, v)
         out.append(c)

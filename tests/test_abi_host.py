@@ -101,6 +101,8 @@ def test_code_payload_equals_m_kv(bits):
     (dict(v_group=48), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(block_size=8), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(v_flush=2), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(v_flush=-1), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(num_blocks=0), kivi.KIVI_ERR_INVALID_ARG),
     (dict(max_seqs=0), kivi.KIVI_ERR_INVALID_ARG),
 ])
