@@ -79,6 +79,20 @@ def lib():
                                                   c.c_int, P, P, c.c_long, P, c.c_int]
             L.orc_attention_raw_chunk.restype = c.c_int
             L.orc_hardware_threads.restype = c.c_int
+            L.orc_e4m3_to_f32.argtypes = [c.c_int]
+            L.orc_e4m3_to_f32.restype = c.c_float
+            L.orc_f32_to_e4m3.argtypes = [c.c_float]
+            L.orc_f32_to_e4m3.restype = c.c_int
+            L.orc_fp8_cache_new.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int, P, P, c.c_int]
+            L.orc_fp8_cache_new.restype = P
+            L.orc_fp8_cache_free.argtypes = [P]
+            L.orc_fp8_cache_append.argtypes = [P, c.c_int, P, P]
+            L.orc_fp8_cache_append.restype = c.c_int
+            L.orc_fp8_cache_len.argtypes = [P]
+            L.orc_fp8_cache_len.restype = c.c_int
+            L.orc_fp8_cache_arrays.argtypes = [P, c.POINTER(P), c.POINTER(P)]
+            L.orc_fp8_attention.argtypes = [P, c.c_int, c.c_int, P, c.c_int, c.c_double, P, c.c_int]
+            L.orc_fp8_attention.restype = c.c_int
             _lib = L
     return _lib
 
@@ -285,3 +299,82 @@ def attention_raw_chunk(caches, H_Q: int, q_bits: np.ndarray, q_dtype: int, cu_q
     if rc != 0:
         raise ValueError("oracle: bad attention arguments")
     return out.reshape(total, H_Q, d) if full else out
+
+
+# --- FP8 (E4M3) cache ("4.4 KV Cache 量化", section 4) -----------------------
+
+def e4m3_to_f32(codes) -> np.ndarray:
+    """float32 value of each E4M3 code (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.int64).ravel()
+    return np.array([lib().orc_e4m3_to_f32(int(x)) for x in c], dtype=np.float32).reshape(np.shape(codes))
+
+
+def f32_to_e4m3(y) -> np.ndarray:
+    """E4M3 code of each float32 value: saturated to +-448, nearest value, ties to the even code."""
+    a = np.asarray(y, dtype=np.float32).ravel()
+    return np.array([lib().orc_f32_to_e4m3(float(x)) for x in a], dtype=np.uint8).reshape(np.shape(y))
+
+
+class Fp8SeqCache:
+    """One request's FP8 cache (one layer, all KV heads): every appended element is stored
+    as E4M3(x / scale) and restored as value * scale. k_scales / v_scales hold one value
+    (per_head=False) or one per KV head."""
+
+    def __init__(self, H, d, dtype, Tmax, k_scales, v_scales, per_head: bool):
+        self.H, self.d, self.dtype, self.Tmax = H, d, dtype, Tmax
+        self._ks = np.ascontiguousarray(k_scales, dtype=np.float32).ravel()
+        self._vs = np.ascontiguousarray(v_scales, dtype=np.float32).ravel()
+        n = H if per_head else 1
+        assert self._ks.size >= n and self._vs.size >= n
+        self._h = lib().orc_fp8_cache_new(H, d, dtype, Tmax, _ptr(self._ks), _ptr(self._vs), 1 if per_head else 0)
+        if not self._h:
+            raise ValueError("oracle: unsupported FP8 cache parameters")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib().orc_fp8_cache_free(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __len__(self):
+        return lib().orc_fp8_cache_len(self._h)
+
+    def append(self, k_bits: np.ndarray, v_bits: np.ndarray):
+        """k_bits, v_bits: [n][H][d] uint16 raw input bits."""
+        k = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+        assert k.shape == v.shape and k.shape[1:] == (self.H, self.d)
+        if lib().orc_fp8_cache_append(self._h, k.shape[0], _ptr(k), _ptr(v)) != 0:
+            raise ValueError("oracle: append beyond Tmax")
+
+    def arrays(self) -> dict:
+        """k_code, v_code: [H][Tmax][d] uint8 views (valid while the cache lives)."""
+        kp, vp = ctypes.c_void_p(), ctypes.c_void_p()
+        lib().orc_fp8_cache_arrays(self._h, ctypes.byref(kp), ctypes.byref(vp))
+        n = self.H * self.Tmax * self.d
+        shape = (self.H, self.Tmax, self.d)
+        out = {}
+        for name, p in (("k_code", kp), ("v_code", vp)):
+            buf = (ctypes.c_uint8 * n).from_address(p.value) if n else None
+            out[name] = (np.frombuffer(buf, dtype=np.uint8) if n else np.zeros(0, np.uint8)).reshape(shape)
+        return out
+
+
+def fp8_attention(caches, H_Q: int, q_bits: np.ndarray, q_dtype: int, sigma: float, threads: int = 1):
+    """Decode attention over FP8 caches, one query row per request at its last position:
+    q_bits [S][H_Q][d] raw bits -> [S][H_Q][d] float64."""
+    S = len(caches)
+    arr = (ctypes.c_void_p * S)(*[c.handle for c in caches])
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    d = caches[0].d
+    assert q.shape == (S, H_Q, d)
+    out = np.zeros((S, H_Q, d), dtype=np.float64)
+    rc = lib().orc_fp8_attention(ctypes.cast(arr, ctypes.c_void_p), S, H_Q, _ptr(q), q_dtype, float(sigma),
+                                 _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad FP8 attention arguments")
+    return out

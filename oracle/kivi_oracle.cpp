@@ -18,7 +18,9 @@
 //        group;
 //      - section 3.2: full-precision residual; Key tokens are quantised in a
 //        batch once enough have accumulated, Value keeps a sliding window of
-//        the newest tokens and quantises the oldest one as each new one comes.
+//        the newest tokens and quantises the oldest one as each new one comes;
+//      - section 4: the FP8 cache (E4M3 on ROCm) with per-tensor or per-KV-head
+//        scales.
 //  * "给 KV cache 减肥" (ai-reference-codex, section 3.1): each K/V pair is
 //    compressed before it is written and restored before the query uses it.
 // Where the pages leave a constant open (rounding, scale formula, dtypes) the
@@ -261,6 +263,76 @@ struct SeqCache {
 };
 
 // ---------------------------------------------------------------------------
+// FP8 KV cache ("4.4 KV Cache 量化", section 4: the cache is stored as FP8;
+// ROCm supports the E4M3 format; a scale brings the values into FP8's range,
+// one per tensor or one per KV head, and is 1.0 when uncalibrated; section
+// 4.5 and "给 KV cache 减肥" section 3: the stored value is restored before
+// attention uses it). No groups and no residual: every token is encoded as it
+// is appended.
+// Readings: E4M3 is the OCP "E4M3FN" layout (sign, 4 exponent bits with bias
+// 7, 3 fraction bits, no infinities, S.1111.111 is NaN, largest finite 448);
+// a stored value is y = fl32(x / scale), saturated to [-448, 448] and rounded
+// to the nearest E4M3 value (ties to the even code); the restored value is
+// fl32(fp8 value * scale).
+// ---------------------------------------------------------------------------
+
+// E4M3 code -> binary32 (exact), from the layout above.
+float e4m3_to_f32(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? m * std::ldexp(1.0, -9) : (1.0 + m / 8.0) * std::ldexp(1.0, e - 7);
+    return (float)(sign ? -mag : mag);
+}
+
+// binary32 -> E4M3: saturate, then the nearest of the 127 non-negative finite
+// values by search (ties to the even code), then the sign. NaN -> 0x7F.
+uint8_t f32_to_e4m3(float y) {
+    if (y != y) return 0x7F;
+    uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
+    double a = std::fabs((double)y);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double err = std::fabs((double)e4m3_to_f32((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) { best = c; best_err = err; }
+    }
+    return (uint8_t)(sign | best);
+}
+
+struct Fp8SeqCache {
+    int H, d, dtype, Tmax;
+    int T = 0;
+    std::vector<float> ks, vs;              // [H] scales (one value repeated per tensor)
+    std::vector<uint8_t> k_code, v_code;    // [H][Tmax][d]
+
+    Fp8SeqCache(int H_, int d_, int dtype_, int Tmax_, const float* k_scales, const float* v_scales, int per_head)
+        : H(H_), d(d_), dtype(dtype_), Tmax(Tmax_), ks(H_), vs(H_),
+          k_code((size_t)H_ * Tmax_ * d_), v_code((size_t)H_ * Tmax_ * d_) {
+        for (int h = 0; h < H; ++h) {
+            ks[h] = k_scales[per_head ? h : 0];
+            vs[h] = v_scales[per_head ? h : 0];
+        }
+    }
+    size_t tok(int h, int t) const { return ((size_t)h * Tmax + t) * d; }
+
+    // Append one token (all heads), k and v [H][d] raw bits: each element is
+    // divided by its head's scale in single precision and encoded.
+    void append_one(const uint16_t* k, const uint16_t* v) {
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < d; ++c) {
+                float xk = load_elem(k[(size_t)h * d + c], dtype);
+                float xv = load_elem(v[(size_t)h * d + c], dtype);
+                k_code[tok(h, T) + c] = f32_to_e4m3(xk / ks[h]);
+                v_code[tok(h, T) + c] = f32_to_e4m3(xv / vs[h]);
+            }
+        ++T;
+    }
+    float k_hat(int h, int t, int c) const { return e4m3_to_f32(k_code[tok(h, t) + c]) * ks[h]; }
+    float v_hat(int h, int t, int c) const { return e4m3_to_f32(v_code[tok(h, t) + c]) * vs[h]; }
+};
+
+// ---------------------------------------------------------------------------
 // Attention over the reconstructed cache ("4.4 KV Cache 量化", section 2:
 // P = softmax(Q K^T / sqrt(d)), output P V; the residual takes part next to
 // the quantised history, section 3.2). fp64 accumulation of fp32 inputs.
@@ -470,6 +542,64 @@ int orc_attention_raw_chunk(void** caches, int S, int H_Q, const uint16_t* q, in
             size_t base = (size_t)cu_q[s] * H * d;
             attend_row_raw_chunk(*c, qf.data(), hq, H_Q, n_chunk, k_chunk + base, v_chunk + base, sigma,
                                  &out[it * d]);
+        }
+    };
+    int nt = threads > 0 ? threads : 1;
+    std::vector<std::thread> pool;
+    for (int i = 1; i < nt; ++i) pool.emplace_back(work);
+    work();
+    for (auto& th : pool) th.join();
+    return 0;
+}
+
+// --- FP8 cache ---------------------------------------------------------------
+float orc_e4m3_to_f32(int c) { return e4m3_to_f32((uint8_t)c); }
+int orc_f32_to_e4m3(float y) { return f32_to_e4m3(y); }
+
+void* orc_fp8_cache_new(int H, int d, int dtype, int Tmax, const float* k_scales, const float* v_scales,
+                        int per_head) {
+    if (H <= 0 || d <= 0 || Tmax < 0 || (dtype != DT_F16 && dtype != DT_BF16) || !k_scales || !v_scales)
+        return nullptr;
+    return new Fp8SeqCache(H, d, dtype, Tmax, k_scales, v_scales, per_head);
+}
+void orc_fp8_cache_free(void* p) { delete static_cast<Fp8SeqCache*>(p); }
+int orc_fp8_cache_append(void* p, int n, const uint16_t* k, const uint16_t* v) {
+    Fp8SeqCache* c = static_cast<Fp8SeqCache*>(p);
+    if (c->T + n > c->Tmax) return -1;
+    for (int i = 0; i < n; ++i) c->append_one(k + (size_t)i * c->H * c->d, v + (size_t)i * c->H * c->d);
+    return 0;
+}
+int orc_fp8_cache_len(void* p) { return static_cast<Fp8SeqCache*>(p)->T; }
+void orc_fp8_cache_arrays(void* p, uint8_t** k_code, uint8_t** v_code) {
+    Fp8SeqCache* c = static_cast<Fp8SeqCache*>(p);
+    *k_code = c->k_code.data();
+    *v_code = c->v_code.data();
+}
+
+// Decode attention over FP8 caches: one query row per request at position
+// T_s - 1, every query head; q [S][H_Q][d] raw bits; out [S][H_Q][d].
+int orc_fp8_attention(void** caches, int S, int H_Q, const uint16_t* q, int q_dtype, double sigma, double* out,
+                      int threads) {
+    if (S <= 0) return -1;
+    for (int s = 0; s < S; ++s) {
+        const Fp8SeqCache* c = static_cast<const Fp8SeqCache*>(caches[s]);
+        if (H_Q % c->H) return -1;
+    }
+    std::atomic<long> next(0);
+    const long n_items = (long)S * H_Q;
+    auto work = [&]() {
+        for (;;) {
+            long it = next.fetch_add(1);
+            if (it >= n_items) break;
+            int s = (int)(it / H_Q), hq = (int)(it % H_Q);
+            const Fp8SeqCache* c = static_cast<const Fp8SeqCache*>(caches[s]);
+            int d = c->d, h = hq / (H_Q / c->H);
+            std::vector<float> qf(d);
+            for (int ch = 0; ch < d; ++ch) qf[ch] = load_elem(q[((size_t)s * H_Q + hq) * d + ch], q_dtype);
+            double* o = &out[it * d];
+            if (c->T == 0) { for (int ch = 0; ch < d; ++ch) o[ch] = 0.0; continue; }
+            attend_tokens(d, qf.data(), c->T, [&](int t, int ch) { return c->k_hat(h, t, ch); },
+                          [&](int t, int ch) { return c->v_hat(h, t, ch); }, sigma, o);
         }
     };
     int nt = threads > 0 ? threads : 1;
