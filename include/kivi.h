@@ -68,7 +68,11 @@ typedef enum kivi_dtype {
 /* Cache configuration (one attention layer).
  *   num_kv_heads  H_KV >= 1
  *   head_dim      must be 128
- *   bits          2 or 4
+ *   bits          2 or 4 (KIVI codes), or 8: the FP8 cache ("4.4 KV Cache 量化",
+ *                 section 4: K and V stored as FP8 E4M3, the format ROCm
+ *                 supports, with no groups and no residual; k_group,
+ *                 v_group, residual and v_flush must then be 0, and only the
+ *                 kivi_fp8_* calls and kivi_decode_workspace_bytes take it)
  *   k_group       G: Key tokens per (channel) group; a multiple of block_size,
  *                 and 128 must be divisible by G/block_size
  *   v_group       Gv: Value channels per (token) group: 16, 32, 64 or 128
@@ -86,7 +90,10 @@ typedef enum kivi_dtype {
  *                 residual tokens are quantised (each per token over Gv
  *                 channels) at every Key flush, so the boundary is
  *                 R*floor(T/R) for both. Any other value is
- *                 KIVI_ERR_UNSUPPORTED. A zero-initialised config takes 0. */
+ *                 KIVI_ERR_UNSUPPORTED. A zero-initialised config takes 0.
+ *   scale_per_head FP8 scale granularity (section 4.2 of the same page): 0 =
+ *                 one Key and one Value scale for the tensor, 1 = one of each
+ *                 per KV head. Must be 0 when bits is 2 or 4.               */
 typedef struct kivi_cache_config {
     int32_t num_kv_heads;
     int32_t head_dim;
@@ -99,6 +106,7 @@ typedef struct kivi_cache_config {
     int32_t max_seqs;
     int32_t kv_dtype;
     int32_t v_flush;
+    int32_t scale_per_head;
 } kivi_cache_config;
 
 /* Byte offsets of the sub-arrays inside the pool (each 256-byte aligned) and
@@ -139,7 +147,17 @@ typedef struct kivi_cache_config {
  *           holds (tile 4w + f/2, token 4j + 2(f%2) + 1).
  * The layout lets a lane turn a 32-bit word into fp16 pairs with one
  * AND-OR per pair (the fp16 bias-exponent trick) and feed matrix cores
- * directly.                                                                  */
+ * directly.
+ *
+ * FP8 cache (bits 8): only K codes and V codes, code_bytes = Bk*128, one
+ * E4M3 byte per element; the meta and ring sub-arrays are empty. Each
+ * 16-token sub-tile (2 KiB) is 64 lane slots of 32 bytes:
+ *   K: slot L = token m, byte 8i + e holds channel 32i + 8j + e
+ *      (i = 0..3, e = 0..7);
+ *   V: slot L = channels {16t + m : t = 0..7}, tokens 4j..4j+3; byte
+ *      4t + r holds (channel 16t + m, token 4j + r).
+ * An E4M3 byte b read as the fp16 bits ((b & 0x80) << 8) | ((b & 0x7F) << 7)
+ * is its value times 2^-8, subnormals included.                              */
 typedef struct kivi_layout {
     uint64_t k_codes, v_codes, k_meta, v_meta, k_ring, v_ring;
     uint64_t total_bytes;
@@ -250,6 +268,37 @@ kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_
                              const void* d_v_new, int32_t max_seq_len, const int32_t* d_block_table,
                              int32_t bt_stride, float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
                              void* stream);
+
+/* Append to an FP8 cache (bits 8): every new K/V element x is stored as
+ * E4M3(x / scale), with x / scale rounded in single precision, saturated to
+ * +-448 and rounded to the nearest E4M3 value, ties to even ("4.4 KV Cache
+ * 量化", section 4.2: the scale brings values into FP8's range).
+ *   d_seq_lens_before[S], d_cu_new[S+1], max_new, d_k_new, d_v_new,
+ *   d_block_table, bt_stride   as for kivi_append_tokens (no residual slots)
+ *   d_k_scale, d_v_scale       device float32 scales, positive and finite:
+ *                              1 value each, or H_KV when scale_per_head
+ * The caller guarantees pages for positions < seq_len_before + n_new.
+ * Errors: INVALID_ARG, UNSUPPORTED (not an FP8 cache), DEVICE.               */
+kivi_status kivi_fp8_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_t* d_seq_lens_before,
+                                   const int32_t* d_cu_new, int32_t max_new, const void* d_k_new,
+                                   const void* d_v_new, const float* d_k_scale, const float* d_v_scale,
+                                   const int32_t* d_block_table, int32_t bt_stride, void* stream);
+
+/* Decode attention over an FP8 cache ("4.4 KV Cache 量化", sections 2 and
+ * 4.5: values are restored, value * scale, before attention uses them; the
+ * attention itself runs in fp32). One query row per sequence at position
+ * T - 1, attending over all T = d_seq_lens[s] tokens.
+ *   d_q[S][H_Q][128] kv_dtype, d_out[S][H_Q][128] kv_dtype
+ *   d_k_scale, d_v_scale       as for kivi_fp8_append_tokens
+ *   d_ws, ws_bytes             kivi_decode_workspace_bytes of this cache
+ * Other arguments as for kivi_decode_attention (no slot ids). A row with
+ * T = 0 writes zeros.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                       */
+kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                      const void* d_q, const int32_t* d_seq_lens, int32_t max_seq_len,
+                                      const float* d_k_scale, const float* d_v_scale,
+                                      const int32_t* d_block_table, int32_t bt_stride, float softmax_scale,
+                                      void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes kivi_prefill_attention needs (0 today; reserved).          */
 kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,

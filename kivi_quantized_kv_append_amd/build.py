@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkivi.so")
-SOURCES = ["kivi_api.cpp", "kivi_append.hip", "kivi_decode.hip", "kivi_prefill.hip"]
+SOURCES = ["kivi_api.cpp", "kivi_append.hip", "kivi_decode.hip", "kivi_prefill.hip", "kivi_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

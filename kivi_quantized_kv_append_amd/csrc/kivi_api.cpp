@@ -43,8 +43,12 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     const kivi_cache_config& c = *cfg;
     if (c.head_dim != kivi::kHeadDim)
         return fail(KIVI_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", c.head_dim);
-    if (c.bits != 2 && c.bits != 4)
-        return fail(KIVI_ERR_UNSUPPORTED, "bits %d unsupported (2 or 4)", c.bits);
+    if (c.bits != 2 && c.bits != 4 && c.bits != 8)
+        return fail(KIVI_ERR_UNSUPPORTED, "bits %d unsupported (2, 4, or 8 for FP8 E4M3)", c.bits);
+    if (c.scale_per_head != 0 && c.scale_per_head != 1)
+        return fail(KIVI_ERR_UNSUPPORTED, "scale_per_head %d unsupported (0 or 1)", c.scale_per_head);
+    if (c.bits != 8 && c.scale_per_head)
+        return fail(KIVI_ERR_UNSUPPORTED, "scale_per_head applies to the FP8 cache (bits 8) only");
     if (c.num_kv_heads < 1 || c.num_kv_heads > 1024)
         return fail(KIVI_ERR_UNSUPPORTED, "num_kv_heads %d outside [1, 1024]", c.num_kv_heads);
     if (c.block_size < 16 || c.block_size > 1024 || c.block_size % 16)
@@ -53,6 +57,30 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     if ((c.block_size & (c.block_size - 1)) || (c.k_group & (c.k_group - 1)))
         return fail(KIVI_ERR_UNSUPPORTED, "block_size %d and k_group %d must be powers of two", c.block_size,
                     c.k_group);
+    if (c.bits == 8) {
+        // FP8: every token is encoded on append; no groups, no residual
+        if (c.k_group || c.v_group || c.residual || c.v_flush)
+            return fail(KIVI_ERR_UNSUPPORTED,
+                        "the FP8 cache has no groups or residual: k_group, v_group, residual and v_flush "
+                        "must be 0");
+        if (c.num_blocks < 1) return fail(KIVI_ERR_INVALID_ARG, "num_blocks %d < 1", c.num_blocks);
+        if (c.max_seqs < 1) return fail(KIVI_ERR_INVALID_ARG, "max_seqs %d < 1", c.max_seqs);
+        if (c.kv_dtype != KIVI_F16 && c.kv_dtype != KIVI_BF16)
+            return fail(KIVI_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c.kv_dtype);
+        const uint64_t H = (uint64_t)c.num_kv_heads;
+        kivi_layout L{};
+        L.code_bytes = (uint64_t)c.block_size * kivi::kHeadDim;
+        uint64_t off = 0;
+        L.k_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
+        L.v_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
+        L.k_meta = L.v_meta = L.k_ring = L.v_ring = off;
+        L.total_bytes = off;
+        if ((uint64_t)c.num_blocks * H * L.code_bytes >= (1ull << 32))
+            return fail(KIVI_ERR_UNSUPPORTED, "code sub-array of %llu bytes exceeds 4 GiB",
+                        (unsigned long long)((uint64_t)c.num_blocks * H * L.code_bytes));
+        if (lay) *lay = L;
+        return KIVI_OK;
+    }
     if (c.k_group < c.block_size || c.k_group % c.block_size || c.k_group > 256)
         return fail(KIVI_ERR_UNSUPPORTED,
                     "k_group %d must be a multiple of block_size %d and at most 256", c.k_group,
@@ -162,6 +190,22 @@ DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int m
 
 namespace {
 
+// Calls of the KIVI codes (bits 2, 4) and of the FP8 cache (bits 8) take only
+// their own kind of cache.
+kivi_status check_kivi_cache(const kivi_cache* cache) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (cache->cfg.bits == 8)
+        return fail(KIVI_ERR_UNSUPPORTED, "an FP8 cache (bits 8) takes the kivi_fp8_* calls");
+    return KIVI_OK;
+}
+kivi_status check_fp8_cache(const kivi_cache* cache) {
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (cache->cfg.bits != 8) return fail(KIVI_ERR_UNSUPPORTED, "not an FP8 cache (bits %d)", cache->cfg.bits);
+    return KIVI_OK;
+}
+
 kivi_status check_heads(const kivi_cache* cache, int32_t num_q_heads) {
     const int H = cache->cfg.num_kv_heads;
     if (num_q_heads < 1) return fail(KIVI_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
@@ -179,7 +223,7 @@ kivi_status prefill_common(const kivi_cache* cache, int32_t num_seqs, int32_t nu
                            const int32_t* d_seq_lens, int32_t max_seq_len, const void* d_k_chunk,
                            const void* d_v_chunk, const int32_t* d_block_table, int32_t bt_stride,
                            float softmax_scale, int32_t causal, void* d_out, void* stream, bool raw_chunk) {
-    kivi_status s = check_cache(cache);
+    kivi_status s = check_kivi_cache(cache);
     if (s != KIVI_OK) return s;
     s = check_heads(cache, num_q_heads);
     if (s != KIVI_OK) return s;
@@ -297,7 +341,7 @@ kivi_status kivi_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_
                                const int32_t* d_seq_lens_before, const int32_t* d_cu_new,
                                int32_t max_new, const void* d_k_new, const void* d_v_new,
                                const int32_t* d_block_table, int32_t bt_stride, void* stream) {
-    kivi_status s = check_cache(cache);
+    kivi_status s = check_kivi_cache(cache);
     if (s != KIVI_OK) return s;
     if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     if (max_new < 0) return fail(KIVI_ERR_INVALID_ARG, "max_new %d < 0", max_new);
@@ -324,7 +368,9 @@ kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seq
     if (num_seqs < 0 || num_q_heads < 1 || max_seq_len < 0)
         return fail(KIVI_ERR_INVALID_ARG, "bad sizes (num_seqs %d, num_q_heads %d, max_seq_len %d)",
                     num_seqs, num_q_heads, max_seq_len);
-    *bytes = kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len).ws_bytes;
+    *bytes = cache->cfg.bits == 8
+                 ? kivi::fp8_decode_plan(num_seqs, cache->cfg.num_kv_heads, num_q_heads, max_seq_len).ws_bytes
+                 : kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len).ws_bytes;
     return ok();
 }
 
@@ -334,7 +380,7 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
                                   const int32_t* d_block_table, int32_t bt_stride,
                                   float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
                                   void* stream) {
-    kivi_status s = check_cache(cache);
+    kivi_status s = check_kivi_cache(cache);
     if (s != KIVI_OK) return s;
     s = check_heads(cache, num_q_heads);
     if (s != KIVI_OK) return s;
@@ -367,7 +413,7 @@ kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_
                              const void* d_v_new, int32_t max_seq_len, const int32_t* d_block_table,
                              int32_t bt_stride, float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
                              void* stream) {
-    kivi_status s = check_cache(cache);
+    kivi_status s = check_kivi_cache(cache);
     if (s != KIVI_OK) return s;
     s = check_heads(cache, num_q_heads);
     if (s != KIVI_OK) return s;
@@ -406,6 +452,61 @@ kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_
                                        d_v_new, d_block_table, bt_stride, softmax_scale, d_out,
                                        static_cast<float*>(d_ws), plan, stream);
     return device_status(err, "decode step launch");
+}
+
+kivi_status kivi_fp8_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_t* d_seq_lens_before,
+                                   const int32_t* d_cu_new, int32_t max_new, const void* d_k_new,
+                                   const void* d_v_new, const float* d_k_scale, const float* d_v_scale,
+                                   const int32_t* d_block_table, int32_t bt_stride, void* stream) {
+    kivi_status s = check_fp8_cache(cache);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_new < 0) return fail(KIVI_ERR_INVALID_ARG, "max_new %d < 0", max_new);
+    if (num_seqs == 0 || max_new == 0) return ok();
+    if (!d_seq_lens_before || !d_cu_new || !d_k_new || !d_v_new || !d_k_scale || !d_v_scale || !d_block_table)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_seq_lens_before, 4) || !aligned(d_cu_new, 4) || !aligned(d_block_table, 4) ||
+        !aligned(d_k_scale, 4) || !aligned(d_v_scale, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 or float array is not 4-byte aligned");
+    if (!aligned(d_k_new, 2) || !aligned(d_v_new, 2))
+        return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 2-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    int err = kivi::launch_fp8_append(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, d_seq_lens_before,
+                                      d_cu_new, max_new, d_k_new, d_v_new, d_k_scale, d_v_scale, d_block_table,
+                                      bt_stride, stream);
+    return device_status(err, "FP8 append launch");
+}
+
+kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                      const void* d_q, const int32_t* d_seq_lens, int32_t max_seq_len,
+                                      const float* d_k_scale, const float* d_v_scale,
+                                      const int32_t* d_block_table, int32_t bt_stride, float softmax_scale,
+                                      void* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+    kivi_status s = check_fp8_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_seq_len < 0) return fail(KIVI_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (!d_q || !d_seq_lens || !d_k_scale || !d_v_scale || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_seq_lens, 4) || !aligned(d_block_table, 4) || !aligned(d_k_scale, 4) || !aligned(d_v_scale, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 or float array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const kivi::Fp8Plan plan = kivi::fp8_decode_plan(num_seqs, cache->cfg.num_kv_heads, num_q_heads, max_seq_len);
+    if (plan.ws_bytes > 0 && (!d_ws || ws_bytes < plan.ws_bytes))
+        return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0, plan.ws_bytes);
+    if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    int err = kivi::launch_fp8_decode(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, num_q_heads, d_q,
+                                      d_seq_lens, d_k_scale, d_v_scale, d_block_table, bt_stride, softmax_scale,
+                                      d_out, static_cast<float*>(d_ws), plan, stream);
+    return device_status(err, "FP8 decode launch");
 }
 
 kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,

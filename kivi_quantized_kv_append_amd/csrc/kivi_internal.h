@@ -90,4 +90,19 @@ int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void
                    const void* v_chunk, const int32_t* block_table, int bt_stride,
                    float softmax_scale, int causal, void* out, void* stream);
 
+// FP8 (E4M3) cache: decode split plan and the kernel launchers.
+struct Fp8Plan {
+    int n_splits;
+    size_t ws_bytes;
+};
+Fp8Plan fp8_decode_plan(int num_seqs, int num_kv_heads, int num_q_heads, int max_seq_len);
+int launch_fp8_append(const CacheView& v, int per_head, int num_seqs, const int32_t* seq_lens_before,
+                      const int32_t* cu_new, int max_new, const void* k_new, const void* v_new,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table, int bt_stride,
+                      void* stream);
+int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
+                      const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                      const int32_t* block_table, int bt_stride, float softmax_scale, void* out, float* partials,
+                      const Fp8Plan& plan, void* stream);
+
 }  // namespace kivi

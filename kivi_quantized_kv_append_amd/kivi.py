@@ -31,6 +31,7 @@ EXPORTED = [
     "kivi_cache_pool_bytes", "kivi_cache_capacity", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
     "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_step",
     "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_prefill_attention_raw_chunk",
+    "kivi_fp8_append_tokens", "kivi_fp8_decode_attention",
     "kivi_last_error",
     "kivi_status_string",
 ]
@@ -45,7 +46,7 @@ class KiviError(RuntimeError):
 class kivi_cache_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_kv_heads", "head_dim", "bits", "k_group", "v_group", "residual", "block_size",
-        "num_blocks", "max_seqs", "kv_dtype", "v_flush")]
+        "num_blocks", "max_seqs", "kv_dtype", "v_flush", "scale_per_head")]
 
 
 class kivi_layout(ctypes.Structure):
@@ -86,6 +87,8 @@ def load():
                                              I32, P, P, S, P]
         L.kivi_prefill_attention_raw_chunk.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, I32, P, I32,
                                                        c.c_float, I32, P, P, S, P]
+        L.kivi_fp8_append_tokens.argtypes = [P, I32, P, P, I32, P, P, P, P, P, I32, P]
+        L.kivi_fp8_decode_attention.argtypes = [P, I32, I32, P, P, I32, P, P, P, I32, c.c_float, P, P, S, P]
         L.kivi_last_error.argtypes = []
         L.kivi_last_error.restype = c.c_char_p
         L.kivi_status_string.argtypes = [c.c_int]
@@ -126,9 +129,16 @@ def _stream(s) -> int | None:
 
 
 def make_config(num_kv_heads, bits, k_group, v_group, residual, block_size, num_blocks, max_seqs,
-                kv_dtype=KIVI_F16, head_dim=128, v_flush=0) -> kivi_cache_config:
+                kv_dtype=KIVI_F16, head_dim=128, v_flush=0, scale_per_head=0) -> kivi_cache_config:
     return kivi_cache_config(num_kv_heads, head_dim, bits, k_group, v_group, residual, block_size,
-                             num_blocks, max_seqs, kv_dtype, v_flush)
+                             num_blocks, max_seqs, kv_dtype, v_flush, scale_per_head)
+
+
+def make_fp8_config(num_kv_heads, block_size, num_blocks, max_seqs=1, kv_dtype=KIVI_F16,
+                    scale_per_head=0) -> kivi_cache_config:
+    """Configuration of an FP8 (E4M3) cache: bits 8, no groups, no residual."""
+    return make_config(num_kv_heads, 8, 0, 0, 0, block_size, num_blocks, max_seqs, kv_dtype,
+                       scale_per_head=scale_per_head)
 
 
 def kivi_cache_pool_bytes(cfg: kivi_cache_config) -> int:
@@ -217,6 +227,22 @@ def kivi_prefill_attention_raw_chunk(cache, num_seqs, num_q_heads, d_q, d_cu_q, 
                                                    _ptr(d_block_table), bt_stride, float(softmax_scale),
                                                    int(causal), _ptr(d_out), _ptr(d_ws), ws_bytes,
                                                    _stream(stream)))
+
+
+def kivi_fp8_append_tokens(cache, num_seqs, d_seq_lens_before, d_cu_new, max_new, d_k_new, d_v_new,
+                           d_k_scale, d_v_scale, d_block_table, bt_stride, stream=None):
+    _check(load().kivi_fp8_append_tokens(cache, num_seqs, _ptr(d_seq_lens_before), _ptr(d_cu_new), max_new,
+                                         _ptr(d_k_new), _ptr(d_v_new), _ptr(d_k_scale), _ptr(d_v_scale),
+                                         _ptr(d_block_table), bt_stride, _stream(stream)))
+
+
+def kivi_fp8_decode_attention(cache, num_seqs, num_q_heads, d_q, d_seq_lens, max_seq_len, d_k_scale, d_v_scale,
+                              d_block_table, bt_stride, softmax_scale, d_out, d_ws=None, ws_bytes=0,
+                              stream=None):
+    _check(load().kivi_fp8_decode_attention(cache, num_seqs, num_q_heads, _ptr(d_q), _ptr(d_seq_lens),
+                                            max_seq_len, _ptr(d_k_scale), _ptr(d_v_scale), _ptr(d_block_table),
+                                            bt_stride, float(softmax_scale), _ptr(d_out), _ptr(d_ws), ws_bytes,
+                                            _stream(stream)))
 
 
 def kivi_last_error() -> str:

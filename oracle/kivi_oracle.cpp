@@ -277,25 +277,38 @@ struct SeqCache {
 // ---------------------------------------------------------------------------
 
 // E4M3 code -> binary32 (exact), from the layout above.
-float e4m3_to_f32(uint8_t c) {
+float e4m3_value(uint8_t c) {
     int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
     if (e == 15 && m == 7) return NAN;
     double mag = (e == 0) ? m * std::ldexp(1.0, -9) : (1.0 + m / 8.0) * std::ldexp(1.0, e - 7);
     return (float)(sign ? -mag : mag);
 }
 
-// binary32 -> E4M3: saturate, then the nearest of the 127 non-negative finite
-// values by search (ties to the even code), then the sign. NaN -> 0x7F.
+// The 256 values, built once from e4m3_value.
+const std::vector<float>& e4m3_table() {
+    static const std::vector<float> t = [] {
+        std::vector<float> v(256);
+        for (int c = 0; c < 256; ++c) v[c] = e4m3_value((uint8_t)c);
+        return v;
+    }();
+    return t;
+}
+float e4m3_to_f32(uint8_t c) { return e4m3_table()[c]; }
+
+// binary32 -> E4M3: saturate, then the nearest of the non-negative finite
+// values (codes 0..0x7E, increasing with the code), ties to the even code,
+// then the sign. NaN -> 0x7F.
 uint8_t f32_to_e4m3(float y) {
     if (y != y) return 0x7F;
     uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
-    double a = std::fabs((double)y);
-    if (a > 448.0) a = 448.0;
-    int best = 0;
-    double best_err = INFINITY;
-    for (int c = 0; c <= 0x7E; ++c) {
-        double err = std::fabs((double)e4m3_to_f32((uint8_t)c) - a);
-        if (err < best_err || (err == best_err && (c & 1) == 0)) { best = c; best_err = err; }
+    float a = std::fabs(y);
+    if (a > 448.0f) a = 448.0f;
+    const float* v = e4m3_table().data();
+    int hi = (int)(std::lower_bound(v, v + 0x7F, a) - v);  // first value >= a
+    int best = hi;
+    if (hi > 0) {
+        double below = (double)a - v[hi - 1], above = (double)v[hi] - a;
+        if (below < above || (below == above && ((hi - 1) & 1) == 0)) best = hi - 1;
     }
     return (uint8_t)(sign | best);
 }

@@ -431,3 +431,122 @@ def check_attention(got_bits: np.ndarray, ref: np.ndarray, dtype: int, atol=2e-3
 
 
 SCALE = 1.0 / math.sqrt(D)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) cache through the kivi_fp8_* calls
+# ---------------------------------------------------------------------------
+
+def amax_scales(w: inputs.Workload, per_head: bool):
+    """Key and Value scales from the workload's own tokens, max|x| / 448 (per KV head or
+    for the tensor): a stand-in for the calibrated scales a checkpoint would carry."""
+    H = w.num_kv_heads
+    km, vm = np.zeros(H), np.zeros(H)
+    for s in range(w.num_seqs):
+        k, v = w.kv_stream(s)
+        if k.shape[0] == 0:
+            continue
+        kf = inputs.bits_to_float(k, w.dtype).astype(np.float64)
+        vf = inputs.bits_to_float(v, w.dtype).astype(np.float64)
+        km = np.maximum(km, np.abs(kf).max(axis=(0, 2)))
+        vm = np.maximum(vm, np.abs(vf).max(axis=(0, 2)))
+    if not per_head:
+        km[:], vm[:] = km.max(), vm.max()
+    return (np.maximum(km, 1e-3) / 448.0).astype(np.float32), (np.maximum(vm, 1e-3) / 448.0).astype(np.float32)
+
+
+def fp8_decode_codes(chunks: np.ndarray, kind: str) -> np.ndarray:
+    """[n_tiles][2048] bytes of 16-token sub-tiles in lane-slot order -> [n_tiles*16][128] codes."""
+    nt = chunks.shape[0]
+    sl = chunks.reshape(nt, 4, 16, 32)  # [tile][j][m][byte]
+    out = np.zeros((nt, 16, D), np.uint8)
+    if kind == "k":  # slot (m, j) byte 8i+e: token m, channel 32i + 8j + e
+        b = sl.reshape(nt, 4, 16, 4, 8)  # [tile][j][m][i][e]
+        out = b.transpose(0, 2, 3, 1, 4).reshape(nt, 16, D)  # [tile][m][(i j e)]
+    else:  # slot (m, j) byte 4t+r: channel 16t + m, token 4j + r
+        b = sl.reshape(nt, 4, 16, 8, 4)  # [tile][j][m][t][r]
+        out = b.transpose(0, 1, 4, 3, 2).reshape(nt, 16, D)  # [tile][(j r)][(t m)]
+    return out.reshape(nt * 16, D)
+
+
+class Fp8GpuCache:
+    """An FP8 cache of a workload's shape (its heads, pages and lengths) on the GPU."""
+
+    def __init__(self, w: inputs.Workload, k_scales, v_scales, per_head: bool, device="cuda"):
+        import torch
+        self.torch, self.w, self.device = torch, w, device
+        self.cfg = kivi.make_fp8_config(w.num_kv_heads, w.block_size, w.num_blocks, 1, w.dtype,
+                                        scale_per_head=int(per_head))
+        self.nbytes = kivi.kivi_cache_pool_bytes(self.cfg)
+        g = torch.Generator(device="cpu").manual_seed(321)
+        self.pool = torch.randint(0, 256, (self.nbytes,), dtype=torch.uint8, generator=g).to(device)
+        self.handle = kivi.kivi_cache_create(self.cfg, self.pool, self.nbytes)
+        self.layout = kivi.kivi_cache_layout(self.handle)
+        self.bt_np = w.block_table()
+        self.bt = torch.from_numpy(self.bt_np).to(device)
+        self.ks = torch.from_numpy(np.ascontiguousarray(k_scales, np.float32)).to(device)
+        self.vs = torch.from_numpy(np.ascontiguousarray(v_scales, np.float32)).to(device)
+        self.lens = np.zeros(w.num_seqs, dtype=np.int64)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            kivi.kivi_cache_destroy(h)
+            self.handle = None
+
+    def t(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+
+    def append(self, rows_k: list, rows_v: list):
+        torch, H = self.torch, self.w.num_kv_heads
+        ns = [r.shape[0] for r in rows_k]
+        cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+        k = np.concatenate(rows_k) if cu[-1] else np.zeros((1, H, D), np.uint16)
+        v = np.concatenate(rows_v) if cu[-1] else np.zeros((1, H, D), np.uint16)
+        kivi.kivi_fp8_append_tokens(self.handle, self.w.num_seqs, self.t(self.lens.astype(np.int32)), self.t(cu),
+                                    int(max(ns)), self.t(k.view(np.int16)), self.t(v.view(np.int16)), self.ks,
+                                    self.vs, self.bt, self.bt.shape[1])
+        self.lens += np.asarray(ns)
+        torch.cuda.synchronize()
+
+    def decode(self, q_bits: np.ndarray, scale: float) -> np.ndarray:
+        torch, S, HQ = self.torch, self.w.num_seqs, self.w.num_q_heads
+        msl = int(self.lens.max())
+        ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, S, HQ, msl)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        out = torch.zeros((S, HQ, D), dtype=torch.int16, device=self.device)
+        kivi.kivi_fp8_decode_attention(self.handle, S, HQ, self.t(np.ascontiguousarray(q_bits).view(np.int16)),
+                                       self.t(self.lens.astype(np.int32)), msl, self.ks, self.vs, self.bt,
+                                       self.bt.shape[1], scale, out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
+    def codes(self, s: int, h: int) -> dict:
+        """The stored K and V codes of sequence s, head h: [T][128] uint8 each."""
+        self.torch.cuda.synchronize()
+        b = self.pool.cpu().numpy()
+        L, T, H, Bk = self.layout, int(self.lens[s]), self.w.num_kv_heads, self.w.block_size
+        cb = L["code_bytes"]
+        pages = [int(x) for x in self.bt_np[s][:(T + Bk - 1) // Bk]]
+        out = {}
+        for name, base in (("k", L["k_codes"]), ("v", L["v_codes"])):
+            ch = np.stack([b[base + (p * H + h) * cb: base + (p * H + h + 1) * cb] for p in pages]) if pages \
+                else np.zeros((0, cb), np.uint8)
+            out[name] = fp8_decode_codes(ch.reshape(-1, 16 * D), name)[:T]
+        return out
+
+
+def fp8_oracle_caches(w: inputs.Workload, k_scales, v_scales, per_head: bool, lens=None, threads: int = 8):
+    """One oracle Fp8SeqCache per request with its first lens[s] tokens (built on threads:
+    the oracle's calls release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lens = w.seq_lens if lens is None else lens
+
+    def build(s):
+        c = oracle.Fp8SeqCache(w.num_kv_heads, D, w.dtype, int(w.final_lens[s]), k_scales, v_scales, per_head)
+        k, v = w.kv_stream(s, 0, int(lens[s]))
+        c.append(k, v)
+        return c
+
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(build, range(w.num_seqs)))

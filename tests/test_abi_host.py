@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "kivi.h")).read()
-    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kivi_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -194,6 +194,77 @@ def test_call_argument_checks_launch_nothing():
                                               None)  # no sequences: a no-op
     finally:
         kivi.kivi_cache_destroy(h)
+
+
+def test_fp8_config_and_layout():
+    """bits 8 is the FP8 (E4M3) cache: no groups, no residual; its code payload is the
+    M_KV formula at 8 bits."""
+    c = kivi.make_fp8_config(8, 16, 2048, scale_per_head=1)
+    n = kivi.kivi_cache_pool_bytes(c)
+    assert n == 2 * 2048 * 8 * 16 * 128
+    assert n == oracle.m_kv_bytes(1, 1, 2048 * 16, 8, 128, 8)
+    h = kivi.kivi_cache_create(c, 1 << 20, n)
+    try:
+        lay = kivi.kivi_cache_layout(h)
+        assert lay["code_bytes"] == 16 * 128 and lay["total_bytes"] == n
+        assert lay["k_meta"] == lay["v_meta"] == lay["k_ring"] == lay["v_ring"] == n
+    finally:
+        kivi.kivi_cache_destroy(h)
+    # density of a 1 GiB budget against fp16 K/V: exactly 2x
+    nb, tokens = kivi.kivi_cache_capacity(kivi.make_fp8_config(8, 16, 1), 1 << 30)
+    assert tokens == (1 << 30) // (2 * 8 * 128)
+
+
+@pytest.mark.parametrize("over", [dict(k_group=64), dict(v_group=128), dict(residual=128), dict(v_flush=1),
+                                  dict(scale_per_head=2)])
+def test_fp8_fail_fast_configs(over):
+    base = dict(num_kv_heads=8, bits=8, k_group=0, v_group=0, residual=0, block_size=16, num_blocks=64,
+                max_seqs=1, kv_dtype=kivi.KIVI_F16)
+    base.update(over)
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.kivi_cache_pool_bytes(kivi.make_config(**base))
+    assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+
+
+def test_scale_granularity_is_fp8_only():
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.kivi_cache_pool_bytes(cfg(scale_per_head=1))
+    assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+
+
+def test_each_cache_kind_takes_only_its_calls():
+    D = 1 << 20
+    h8 = kivi.kivi_cache_create(kivi.make_fp8_config(8, 16, 64), D, 1 << 40)
+    h4 = kivi.kivi_cache_create(cfg(), D, 1 << 40)
+    try:
+        for call in (lambda: kivi.kivi_append_tokens(h8, 2, D, D, D, 1, D, D, D, 1),
+                     lambda: kivi.kivi_decode_attention(h8, 2, 32, D, D, D, 64, D, 1, 0.1, D, D, 1 << 20),
+                     lambda: kivi.kivi_decode_step(h8, 2, 32, D, D, D, D, D, 64, D, 1, 0.1, D, D, 1 << 20),
+                     lambda: kivi.kivi_prefill_attention(h8, 2, 32, D, D, 16, D, D, 64, D, 1, 0.1, 1, D),
+                     lambda: kivi.kivi_fp8_append_tokens(h4, 2, D, D, 1, D, D, D, D, D, 1),
+                     lambda: kivi.kivi_fp8_decode_attention(h4, 2, 32, D, D, 64, D, D, D, 1, 0.1, D, D, 1 << 20)):
+            with pytest.raises(kivi.KiviError) as e:
+                call()
+            assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+        # FP8 argument checks before any launch
+        kivi.kivi_fp8_append_tokens(h8, 0, None, None, 0, None, None, None, None, None, 1)  # no-op
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_append_tokens(h8, 2, D, D, 1, D, D, None, D, D, 1)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        ws = kivi.kivi_decode_workspace_bytes(h8, 4, 32, 32768)
+        assert ws > 0
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_attention(h8, 4, 32, D, D, 32768, D, D, D, 1, 0.1, D, D, ws - 1)
+        assert e.value.status == kivi.KIVI_ERR_WORKSPACE
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_attention(h8, 4, 30, D, D, 32768, D, D, D, 1, 0.1, D, D, ws)
+        assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_attention(h8, 4, 32, D + 8, D, 32768, D, D, D, 1, 0.1, D, D, ws)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+    finally:
+        kivi.kivi_cache_destroy(h8)
+        kivi.kivi_cache_destroy(h4)
 
 
 def test_status_strings():

@@ -1,0 +1,87 @@
+"""GPU parity of the FP8 (E4M3) cache (kivi_fp8_append_tokens, kivi_fp8_decode_attention)
+against the CPU oracle, through the C ABI: every stored byte bit for bit, decode
+attention within |o - r| <= 2e-3 + 1e-2 |r|.
+
+Scales are max|x| / 448 of each workload's own tokens (per tensor or per KV head), a
+stand-in for calibrated checkpoint scales; one case uses scale 1.0, the uncalibrated
+default, where large values saturate."""
+import math
+
+import numpy as np
+import pytest
+
+from kivi_quantized_kv_append_amd import inputs
+from harness import SCALE, Fp8GpuCache, amax_scales, check_attention, fp8_oracle_caches
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare_codes(gc, orcs, heads=None):
+    for s, c in enumerate(orcs):
+        a = c.arrays()
+        T = len(c)
+        for h in (range(gc.w.num_kv_heads) if heads is None else heads):
+            got = gc.codes(s, h)
+            assert np.array_equal(got["k"], a["k_code"][h, :T]), f"K codes seq {s} head {h}"
+            assert np.array_equal(got["v"], a["v_code"][h, :T]), f"V codes seq {s} head {h}"
+
+
+def _case(w, per_head, plan=None, scales=None, heads=None, step=0):
+    """Append every stream (in chunks per plan: tokens per call), compare codes and decode."""
+    ks, vs = scales if scales is not None else amax_scales(w, per_head)
+    gc = Fp8GpuCache(w, ks, vs, per_head)
+    streams = [w.kv_stream(s) for s in range(w.num_seqs)]
+    pos = np.zeros(w.num_seqs, dtype=np.int64)
+    for n in (plan or [int(w.final_lens.max())]):
+        ns = [int(min(n, w.final_lens[s] - pos[s])) for s in range(w.num_seqs)]
+        gc.append([streams[s][0][pos[s]:pos[s] + ns[s]] for s in range(w.num_seqs)],
+                  [streams[s][1][pos[s]:pos[s] + ns[s]] for s in range(w.num_seqs)])
+        pos += np.asarray(ns)
+    orcs = fp8_oracle_caches(w, ks, vs, per_head, lens=pos)
+    _compare_codes(gc, orcs, heads)
+    q = w.q_decode(step)
+    got = gc.decode(q, SCALE)
+    ref = oracle.fp8_attention(orcs, w.num_q_heads, q, w.dtype, SCALE, threads=8)
+    return check_attention(got, ref, w.dtype, label=f"{w.name} fp8 per_head={per_head}")
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_fp8_tiny_stream_of_appends(per_head):
+    """One request, 4 query heads over 1 KV head: single tokens, then bulk appends
+    across tile and page edges."""
+    w = inputs.config(1, bits=4)
+    _case(w, per_head, plan=[1] * 20 + [7, 33, 64, 1, 1, 130])
+
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+def test_fp8_ragged_llama_shape(dtype):
+    """32 Q / 8 KV heads, lengths at tile edges (including empty and one-token requests),
+    shuffled pages of 32 tokens."""
+    lens = [0, 1, 15, 16, 17, 127, 1000, 2049]
+    w = inputs.config(2, num_seqs=len(lens), seq_lens=lens, shuffle=True, pool_factor=1.25, block_size=32,
+                      dtype=dtype)
+    _case(w, per_head=True, plan=[5, 300, 4000])
+
+
+@pytest.mark.parametrize("gqa", [1, 7, 16])
+def test_fp8_gqa_and_splits(gqa):
+    """Few long requests: the attention is split over work groups and merged."""
+    w = inputs.config(3, num_seqs=2, seq_lens=[6000, 3333], num_kv_heads=2, num_q_heads=2 * gqa)
+    _case(w, per_head=False)
+
+
+def test_fp8_scale_one_saturates():
+    """Scale 1.0 (the uncalibrated default) with Keys whose outlier channels pass 448."""
+    w = inputs.config(1, bits=4, n_outlier=4, outlier_scale=600.0, seq_lens=[200])
+    ks = np.ones(1, np.float32)
+    k, _ = w.kv_stream(0)
+    assert np.abs(inputs.bits_to_float(k, w.dtype)).max() > 448
+    _case(w, per_head=False, scales=(ks, ks), plan=[77, 123])
+
+
+def test_fp8_llama_decode_full_size():
+    """Llama-3-8B decode layer at full size (32 requests x 4096 tokens, 32 Q / 8 KV), codes of
+    two heads compared, every output against the oracle."""
+    w = inputs.config(2)
+    _case(w, per_head=True, heads=(0, 5))
