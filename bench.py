@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--separate-calls", action="store_true",
                     help="time the step as kivi_append_tokens + kivi_decode_attention instead of kivi_decode_step")
     ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the tiny, long-context, ragged-stream and FP8 measurements")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the timed steps "
                          "(a known-size kernel for scaling hardware byte counters)")
@@ -177,6 +179,222 @@ def prefill_leg(torch, kivi, inputs, dev, n_iter: int, check: bool):
         res["parity"] = {"sampled_rows": int(rows.size), "max_abs": float(err.max()),
                          "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
     kivi.kivi_cache_destroy(h)
+    return res
+
+
+def fp8_decode_bytes(lens, H, g, block_size) -> int:
+    """Algorithmic bytes of one FP8 decode call: one byte per K and V element, q and out."""
+    d, es = 128, 2
+    return sum(int(T) * d * 2 * H + 2 * g * d * es * H + 4 * math.ceil(int(T) / block_size) for T in lens)
+
+
+def _back_to_back_us(torch, stream, calls, runs: int = 3) -> float:
+    """Mean microseconds per call of `calls` (a list of closures) issued back to back,
+    one HIP event pair around the whole run on `stream`; mean over `runs` runs."""
+    out = []
+    with torch.cuda.stream(stream):
+        for c in calls[:2]:
+            c()
+        for _ in range(runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for c in calls:
+                c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+    return float(np.mean(out))
+
+
+def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 100):
+    """kivi_decode_attention on workload cfg_id (every token already appended), launched back
+    to back over replica caches that together exceed the last-level cache."""
+    w = inputs.config(cfg_id, bits=bits)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    streams = w.kv_streams()
+    lens = w.seq_lens.astype(np.int64)
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    nbytes = decode_bytes(lens, w)
+    n_rep = int(min(8, max(1, math.ceil(2 * MALL_BYTES / nbytes))))
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, w.num_blocks, S, w.dtype)
+    pool_bytes = kivi.kivi_cache_pool_bytes(cfg)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    dk = dev_u16(np.concatenate([streams[s][0] for s in range(S)]))
+    dv = dev_u16(np.concatenate([streams[s][1] for s in range(S)]))
+    pools, handles = [], []
+    for _ in range(n_rep):
+        p = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        h = kivi.kivi_cache_create(cfg, p, pool_bytes)
+        kivi.kivi_append_tokens(h, S, slots, zeros, cu, int(lens.max()), dk, dv, bt, bt.shape[1])
+        pools.append(p)
+        handles.append(h)
+    torch.cuda.synchronize()
+    del dk, dv
+    q = dev_u16(w.q_decode(0))
+    lens_dev = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    msl = int(lens.max())
+    ws_bytes = kivi.kivi_decode_workspace_bytes(handles[0], S, HQ, msl)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(d)
+    calls = [lambda h=handles[i % n_rep]: kivi.kivi_decode_attention(
+        h, S, HQ, q, slots, lens_dev, msl, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
+        for i in range(n_calls)]
+    us = _back_to_back_us(torch, stream, calls)
+    for h in handles:
+        kivi.kivi_cache_destroy(h)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": w.name, "bits": bits, "num_seqs": S, "seq_len": int(lens.max()), "replicas": n_rep,
+            "decode_us": round(us, 2), "bytes_per_call": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "kv_tokens_per_s": round(float(lens.sum()) / (us * 1e-6), 1),
+            "note": "back-to-back kivi_decode_attention calls (split-K decode + merge when split), "
+                    "one HIP event pair"}
+
+
+def stream_leg(torch, kivi, inputs, dev, n_steps: int = 64):
+    """The ragged streaming batch: 256 requests of U{128..8192} tokens, then n_steps
+    kivi_decode_step calls (append one token per request, attend), timed as one run."""
+    w = inputs.config(4)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    streams = w.kv_streams()
+    lens = w.seq_lens.astype(np.int64)
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, w.num_blocks, S, w.dtype)
+    pool_bytes = kivi.kivi_cache_pool_bytes(cfg)
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    h = kivi.kivi_cache_create(cfg, pool, pool_bytes)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    dk = dev_u16(np.concatenate([streams[s][0][:lens[s]] for s in range(S)]))
+    dv = dev_u16(np.concatenate([streams[s][1][:lens[s]] for s in range(S)]))
+    kivi.kivi_append_tokens(h, S, slots, zeros, cu, int(lens.max()), dk, dv, bt, bt.shape[1])
+    torch.cuda.synchronize()
+    del dk, dv
+    step_k = [dev_u16(np.stack([streams[s][0][lens[s] + i] for s in range(S)])) for i in range(n_steps)]
+    step_v = [dev_u16(np.stack([streams[s][1][lens[s] + i] for s in range(S)])) for i in range(n_steps)]
+    step_q = [dev_u16(w.q_decode(i)) for i in range(n_steps)]
+    lens_before = [torch.from_numpy((lens + i).astype(np.int32)).to(dev) for i in range(n_steps)]
+    msl = int(lens.max()) + n_steps
+    ws_bytes = kivi.kivi_decode_workspace_bytes(h, S, HQ, msl)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(d)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_steps):
+            kivi.kivi_decode_step(h, S, HQ, step_q[i], slots, lens_before[i], step_k[i], step_v[i], msl, bt,
+                                  bt.shape[1], scale, out, ws, ws_bytes, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n_steps
+    kivi.kivi_cache_destroy(h)
+    nbytes = float(np.mean([decode_bytes(lens + i + 1, w) for i in range(n_steps)]))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": w.name, "num_seqs": S, "tokens_before": int(lens.sum()), "steps": n_steps,
+            "step_us": round(us, 2), "bytes_per_step": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "kv_tokens_per_s": round(float(np.mean([(lens + i + 1).sum() for i in range(n_steps)])) / (us * 1e-6), 1),
+            "note": "kivi_decode_step calls (append with evictions and flushes, attention) back to back, "
+                    "one HIP event pair around all steps"}
+
+
+def fp8_leg(torch, kivi, inputs, dev, int4_decode_us: float, check: bool, n_calls: int = 100):
+    """The FP8 (E4M3) cache on the Llama-3-8B decode workload (32 x 4096 tokens, 32 Q / 8 KV
+    heads, per-head scales max|x|/448 of the data): kivi_fp8_decode_attention back to back,
+    against the int4 decode of the same workload."""
+    w = inputs.config(2)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    streams = w.kv_streams()
+    lens = w.seq_lens.astype(np.int64)
+    km, vm = np.zeros(H), np.zeros(H)
+    for s in range(S):
+        km = np.maximum(km, np.abs(inputs.bits_to_float(streams[s][0], w.dtype)).max(axis=(0, 2)))
+        vm = np.maximum(vm, np.abs(inputs.bits_to_float(streams[s][1], w.dtype)).max(axis=(0, 2)))
+    ks, vs = (km / 448.0).astype(np.float32), (vm / 448.0).astype(np.float32)
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    nbytes = fp8_decode_bytes(lens, H, HQ // H, w.block_size)
+    n_rep = int(min(8, max(1, math.ceil(2 * MALL_BYTES / nbytes))))
+    cfg = kivi.make_fp8_config(H, w.block_size, w.num_blocks, 1, w.dtype, scale_per_head=1)
+    pool_bytes = kivi.kivi_cache_pool_bytes(cfg)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    dk = dev_u16(np.concatenate([streams[s][0] for s in range(S)]))
+    dv = dev_u16(np.concatenate([streams[s][1] for s in range(S)]))
+    dks, dvs = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+    pools, handles = [], []
+    for _ in range(n_rep):
+        p = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        h = kivi.kivi_cache_create(cfg, p, pool_bytes)
+        kivi.kivi_fp8_append_tokens(h, S, zeros, cu, int(lens.max()), dk, dv, dks, dvs, bt, bt.shape[1])
+        pools.append(p)
+        handles.append(h)
+    torch.cuda.synchronize()
+    del dk, dv
+    q_bits = w.q_decode(0)
+    q = dev_u16(q_bits)
+    lens_dev = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    msl = int(lens.max())
+    ws_bytes = kivi.kivi_decode_workspace_bytes(handles[0], S, HQ, msl)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(d)
+    calls = [lambda h=handles[i % n_rep]: kivi.kivi_fp8_decode_attention(
+        h, S, HQ, q, lens_dev, msl, dks, dvs, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
+        for i in range(n_calls)]
+    us = _back_to_back_us(torch, stream, calls)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {"workload": w.name, "format": "e4m3", "scales": "per KV head, max|x|/448", "replicas": n_rep,
+           "decode_us": round(us, 2), "bytes_per_call": int(nbytes),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernel": "fp8_decode_kernel (+ fp8_merge_kernel): one kivi_fp8_decode_attention call"},
+           "kv_tokens_per_s": round(float(lens.sum()) / (us * 1e-6), 1),
+           "int4_decode_us": round(int4_decode_us, 2),
+           "fp8_over_int4_time": round(us / int4_decode_us, 3)}
+    if check:
+        import oracle
+        kivi.kivi_fp8_decode_attention(handles[0], S, HQ, q, lens_dev, msl, dks, dvs, bt, bt.shape[1], scale, out,
+                                       ws, ws_bytes)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        sample = 4
+        caches = []
+        for s in range(sample):
+            c = oracle.Fp8SeqCache(H, d, w.dtype, int(lens[s]), ks, vs, True)
+            c.append(streams[s][0], streams[s][1])
+            caches.append(c)
+        ref = oracle.fp8_attention(caches, HQ, q_bits[:sample], w.dtype, scale, threads=oracle.hardware_threads())
+        g32 = inputs.bits_to_float(got[:sample], w.dtype).astype(np.float64)
+        r32 = ref.astype(np.float32).astype(np.float64)
+        err = np.abs(g32 - r32)
+        res["parity"] = {"requests": sample, "max_abs": float(err.max()),
+                         "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
+    for h in handles:
+        kivi.kivi_cache_destroy(h)
     return res
 
 
@@ -487,6 +705,15 @@ def main():
     del pools, step_k, step_v, step_q
     if not args.no_prefill:
         res["prefill"] = prefill_leg(torch, kivi, inputs, dev, args.prefill_iters, not args.no_cpu_baseline)
+    if not args.no_other_workloads:
+        # the other workloads of the decode path, each on its own caches
+        others = [decode_leg(torch, kivi, inputs, dev, 1, 4), decode_leg(torch, kivi, inputs, dev, 1, 2)]
+        if args.config != 3:
+            others += [decode_leg(torch, kivi, inputs, dev, 3, 4), decode_leg(torch, kivi, inputs, dev, 3, 2)]
+        res["other_workloads"] = others
+        res["ragged_stream"] = stream_leg(torch, kivi, inputs, dev)
+        if args.config == 2 and args.bits == 4:
+            res["fp8"] = fp8_leg(torch, kivi, inputs, dev, float(launch_ms.mean()) * 1e3, not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
