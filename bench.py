@@ -371,6 +371,7 @@ def fp8_leg(torch, kivi, inputs, dev, int4_decode_us: float, check: bool, n_call
            "decode_us": round(us, 2), "bytes_per_call": int(nbytes),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(w.name, "fp8_decode_kernel"),
                         "kernel": "fp8_decode_kernel (+ fp8_merge_kernel): one kivi_fp8_decode_attention call"},
            "kv_tokens_per_s": round(float(lens.sum()) / (us * 1e-6), 1),
            "int4_decode_us": round(int4_decode_us, 2),
@@ -432,10 +433,10 @@ def measured_mfma_util(workload: str):
     return None
 
 
-def measured_traffic(cfg_name: str):
-    """HBM bytes per decode launch from committed rocprofv3 PMC summaries, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.txt" % cfg_name)
+def measured_traffic(cfg_name: str, prefix: str = "decode_traffic"):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they were taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s.txt" % (prefix, cfg_name))
     if not os.path.exists(path):
         return None
     vals = {}
