@@ -12,11 +12,12 @@
 // reads.
 //
 // Decode: one work group of 4 waves per (sequence, KV head, split); each wave
-// streams a contiguous run of 16-token tiles with one tile in flight while it
-// computes the previous one. An E4M3 byte becomes the fp16 number value*2^-8
+// streams a contiguous run of 16-token tiles, one buffer of kF8BufTiles tiles
+// in flight while it computes the other. An E4M3 byte becomes the fp16 number value*2^-8
 // with one byte permute and two masks (exact, subnormals included), so the
 // scores S[16 tok][16 heads] = K x q^T are 4 v_mfma_f32_16x16x32_f16 and the
-// values O^T[128][16] += V^T x P are 8 more, P split into fp16 hi + lo. The
+// values O^T[128][16] += V^T x P are 8 more, P split into fp16 hi + lo; the
+// running max moves lazily, as in the KIVI decode kernel. The
 // Key scale (times 2^8) folds into the softmax scale and the Value scale into
 // the output. The waves merge (m, l, o) in LDS; with several splits a merge
 // kernel combines the partials.
@@ -34,6 +35,7 @@ constexpr int kF8Threads = 256;
 constexpr int kF8Waves = 4;
 constexpr int kF8TileBytes = kTile * kHeadDim;  // 2 KiB: 64 lane slots of 32 bytes
 constexpr int kF8MinSplitTiles = 32;
+constexpr int kF8BufTiles = 1;  // tiles per load buffer (two buffers per wave); 2 and 4 measured slower
 
 // ---------------------------------------------------------------- append ---
 
@@ -124,10 +126,13 @@ struct F8DecodeArgs {
 };
 
 // fp16 pair (value(b_lo) 2^-8, value(b_hi) 2^-8) of two E4M3 bytes of w picked
-// by sel (v_perm selectors placing them in bits 0..7 and 16..23).
+// by sel (v_perm selectors placing them in bits 0..7 and 16..23). Adding the
+// sign bits to themselves moves each one bit up (no carry reaches the next
+// field), so one shift by 7 then places sign, exponent and fraction:
+// ((b & 0x80) << 8) | ((b & 0x7F) << 7) per half, in three instructions.
 __device__ __forceinline__ uint32_t f8_pair(uint32_t w, uint32_t sel) {
     const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
-    return ((x & 0x00800080u) << 8) | ((x & 0x007F007Fu) << 7);
+    return (x + (x & 0x00800080u)) << 7;
 }
 constexpr uint32_t kSel01 = 0x0c010c00u, kSel23 = 0x0c030c02u;
 
@@ -234,13 +239,22 @@ __global__ __launch_bounds__(kF8Threads) void fp8_decode_kernel(F8DecodeArgs a) 
             xr[r] = p0 + r < T ? acc[r] * xs : -INFINITY;
             mx = fmaxf(mx, xr[r]);
         }
-        const float m_new = fmaxf(m_run, xor_max(mx));  // finite: the tile holds a token < T
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
+        // The running max moves only when a score passes it by more than
+        // kLazyLog2 (weights stay below 2^kLazyLog2), so the accumulators are
+        // rescaled rarely; the branch is taken by the whole wave or not at all.
+        const float mt = xor_max(mx);  // finite: the tile holds a token < T
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazyLog2) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
+            l_acc *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) O[tt] *= alpha;
+            m_run = m_new;
+        }
         float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(xr[r] - m_new);
-        m_run = m_new;
-        l_acc = l_acc * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(xr[r] - m_run);
+        l_acc += (p[0] + p[1]) + (p[2] + p[3]);
         h8 B;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -253,19 +267,25 @@ __global__ __launch_bounds__(kF8Threads) void fp8_decode_kernel(F8DecodeArgs a) 
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
             const h4 A = make_h4(f8_pair(vw[tt], kSel01), f8_pair(vw[tt], kSel23));
-            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, O[tt] * alpha, 0, 0, 0);
+            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, O[tt], 0, 0, 0);
         }
     };
 
     if (w_begin < w_end) {
-        F8Tile xa, xb;
-        issue(w_begin, xa);
-        for (int t = w_begin; t < w_end; t += 2) {
-            issue(t + 1, xb);
-            compute(xa, t);
-            if (t + 1 >= w_end) break;
-            issue(t + 2, xa);
-            compute(xb, t + 1);
+        constexpr int NB = kF8BufTiles;
+        F8Tile xa[NB], xb[NB];
+#pragma unroll
+        for (int e = 0; e < NB; ++e) issue(w_begin + e, xa[e]);
+        for (int t = w_begin; t < w_end; t += 2 * NB) {
+#pragma unroll
+            for (int e = 0; e < NB; ++e) issue(t + NB + e, xb[e]);
+#pragma unroll
+            for (int e = 0; e < NB; ++e) compute(xa[e], t + e);
+            if (t + NB >= w_end) break;
+#pragma unroll
+            for (int e = 0; e < NB; ++e) issue(t + 2 * NB + e, xa[e]);
+#pragma unroll
+            for (int e = 0; e < NB; ++e) compute(xb[e], t + NB + e);
         }
     }
 
