@@ -35,6 +35,7 @@ constexpr int kF8Threads = 256;
 constexpr int kF8Waves = 4;
 constexpr int kF8TileBytes = kTile * kHeadDim;  // 2 KiB: 64 lane slots of 32 bytes
 constexpr int kF8MinSplitTiles = 32;
+constexpr int kF8ResidentGroups = 1024;  // 4-wave work groups resident at once (4 per CU)
 constexpr int kF8BufTiles = 1;  // tiles per load buffer (two buffers per wave); 2 and 4 measured slower
 
 // ---------------------------------------------------------------- append ---
@@ -141,8 +142,11 @@ struct F8Tile {
     bool ok;
 };
 
+// The second bound lets the compiler keep every value in 128 VGPRs (four
+// waves per SIMD); without it the accumulators are parked in AGPRs and copied
+// back each tile.
 template <int DT>
-__global__ __launch_bounds__(kF8Threads) void fp8_decode_kernel(F8DecodeArgs a) {
+__global__ __launch_bounds__(kF8Threads, 2) void fp8_decode_kernel(F8DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int split = blockIdx.x % a.n_splits;
     const int sh = blockIdx.x / a.n_splits;
@@ -360,9 +364,9 @@ __global__ __launch_bounds__(kHeadDim) void fp8_merge_kernel(const float* partia
 Fp8Plan fp8_decode_plan(int num_seqs, int num_kv_heads, int num_q_heads, int max_seq_len) {
     const int pairs = std::max(1, num_seqs * num_kv_heads);
     const int tiles = (std::max(0, max_seq_len) + kTile - 1) / kTile;
-    // about three resident 4-wave work groups per CU on 256 CUs, at least
+    // about four resident 4-wave work groups per CU on 256 CUs, at least
     // kF8MinSplitTiles tiles per split
-    int n_splits = std::max(1, (768 + pairs / 2) / pairs);
+    int n_splits = std::max(1, (kF8ResidentGroups + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (tiles + kF8MinSplitTiles - 1) / kF8MinSplitTiles));
     n_splits = std::max(1, std::min(n_splits, 256));
     Fp8Plan p;
