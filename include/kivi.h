@@ -117,10 +117,12 @@ typedef struct kivi_cache_config {
  *   K meta   [num_blocks][H_KV][k_meta_bytes] k_meta_bytes = 4*128*Bk/G
  *   V meta   [num_blocks][H_KV][Bk][128/Gv][2] fp16 (scale, zero)
  *   K ring   [max_seqs][H_KV][R][128]  kv_dtype, token-major
- *   V ring   [max_seqs][H_KV][128][R]  kv_dtype, channel-major
+ *   V ring   [max_seqs][H_KV][R/4][128][4]  kv_dtype: quads of 4 ring rows,
+ *            channel-major inside a quad
  *
  * A token at position p of a sequence lives in page block_table[p / Bk], row
- * p % Bk; in the residual it lives in ring row (K) / column (V) p % R.
+ * p % Bk; in the residual it lives in ring row r = p % R: K ring row r, V
+ * ring quad r / 4, element [channel][r % 4].
  *
  * K meta: the G/Bk pages of Key group j (tokens jG .. jG+G-1) each hold the
  * pairs of nch = 128*Bk/G channels: page i of the group holds channels

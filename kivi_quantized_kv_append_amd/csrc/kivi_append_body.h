@@ -76,7 +76,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
     const int bt_len = a.bt_stride;
 
     uint16_t* ringK = V.k_ring + ((size_t)slot * H + h) * V.ring_elems;  // [R][128]
-    uint16_t* ringV = V.v_ring + ((size_t)slot * H + h) * V.ring_elems;  // [128][R]
+    uint16_t* ringV = V.v_ring + ((size_t)slot * H + h) * V.ring_elems;  // [R/4][128][4]
     const size_t in_stride = (size_t)H * kHeadDim;
     const uint16_t* inK = a.k_new + (size_t)row0 * in_stride + (size_t)h * kHeadDim;
     const uint16_t* inV = a.v_new + (size_t)row0 * in_stride + (size_t)h * kHeadDim;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
         return canon(to_f32<DT>(u));
     };
     auto vval = [&](int p, int c) -> float {
-        uint16_t u = p < T0 ? ringV[(size_t)c * R + (p % R)] : inV[(size_t)(p - T0) * in_stride + c];
+        uint16_t u = p < T0 ? ringV[vring_index(R, p, c)] : inV[(size_t)(p - T0) * in_stride + c];
         return canon(to_f32<DT>(u));
     };
 
@@ -291,7 +291,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
         const int nk = T1 - k_first, nv = T1 - v_first;
         if (one_row) {  // the row is at position T0 (nk, nv <= 1)
             if (nk > 0 && tid < 16) *reinterpret_cast<uint4*>(ringK + (size_t)(T0 % R) * kHeadDim + 8 * tid) = row_k;
-            if (nv > 0 && tid < kHeadDim) ringV[(size_t)tid * R + (T0 % R)] = row_v;
+            if (nv > 0 && tid < kHeadDim) ringV[vring_index(R, T0, tid)] = row_v;
             return;
         }
         // Key ring: token-major rows, 16-byte chunks
@@ -300,10 +300,10 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
             const uint4 val = *reinterpret_cast<const uint4*>(inK + (size_t)(p - T0) * in_stride + ch);
             *reinterpret_cast<uint4*>(ringK + (size_t)(p % R) * kHeadDim + ch) = val;
         }
-        // Value ring: channel-major
+        // Value ring: quads of [128 channels][4 tokens]
         for (int q = tid; q < nv * kHeadDim; q += NT) {
-            const int ch = q / nv, p = v_first + q % nv;
-            ringV[(size_t)ch * R + (p % R)] = inV[(size_t)(p - T0) * in_stride + ch];
+            const int p = v_first + q / kHeadDim, ch = q % kHeadDim;
+            ringV[vring_index(R, p, ch)] = inV[(size_t)(p - T0) * in_stride + ch];
         }
     }
 }
@@ -385,8 +385,8 @@ __device__ __forceinline__ void append_token_value_wave(const AppendArgs& a, int
     const uint32_t vv = *reinterpret_cast<const uint32_t*>(t.inV + 2 * lane);
     if (TV1 > TV0) {  // token p leaves the window (its ring slot is the new token's)
         const int p = TV0;
-        const float x0 = canon(to_f32<DT>(t.ringV[(size_t)(2 * lane) * R + p % R]));
-        const float x1 = canon(to_f32<DT>(t.ringV[(size_t)(2 * lane + 1) * R + p % R]));
+        const float x0 = canon(to_f32<DT>(t.ringV[vring_index(R, p, 2 * lane)]));
+        const float x1 = canon(to_f32<DT>(t.ringV[vring_index(R, p, 2 * lane + 1)]));
         const int gw = t.Gv / 2;  // lanes per channel group
         const float mn = group_min(fminf(x0, x1), gw);
         const float mx = group_max(fmaxf(x0, x1), gw);
@@ -434,8 +434,8 @@ __device__ __forceinline__ void append_token_value_wave(const AppendArgs& a, int
     }
     // residual writes (after the read above of the same Value slot)
     if (TK1 <= T0) *reinterpret_cast<uint32_t*>(t.ringK + (size_t)slot_new * kHeadDim + 2 * lane) = kv;
-    t.ringV[(size_t)(2 * lane) * R + slot_new] = (uint16_t)(vv & 0xFFFFu);
-    t.ringV[(size_t)(2 * lane + 1) * R + slot_new] = (uint16_t)(vv >> 16);
+    t.ringV[vring_index(R, slot_new, 2 * lane)] = (uint16_t)(vv & 0xFFFFu);
+    t.ringV[vring_index(R, slot_new, 2 * lane + 1)] = (uint16_t)(vv >> 16);
 }
 
 template <int BITS, int DT>

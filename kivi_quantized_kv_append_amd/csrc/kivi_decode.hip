@@ -344,11 +344,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             }
         }
         // residual Values: positions 4j..4j+3 of a channel are adjacent in the
-        // channel-major ring (R is a multiple of 16, so they never wrap)
+        // ring's quads (R is a multiple of 16, so they never wrap)
         const int pq = p0 + 4 * j;
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
-            x.vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
+            x.vr[tt] = *reinterpret_cast<const uint2*>(ringV + vring_index(R, pq, 16 * tt + n));
         if (a.fuse && pq <= T - 1 && T - 1 < pq + 4) {  // a fused step's own token from its input row
             const uint16_t* vrow = a.app.v_new + ((size_t)c.s * H + c.h) * kHeadDim;
             const int r = T - 1 - pq, sh16 = 16 * (r & 1);

@@ -33,6 +33,14 @@ struct CacheView {
     int vflush;  // 0: sliding Value window; 1: Values flush with the Keys
 };
 
+// Element (position p, channel c) of a Value ring of R tokens: ring rows in
+// quads, each quad [128 channels][4 tokens], so a channel's 4 tokens of a
+// quad are 8 contiguous bytes and one token's 128 channels span 1 KiB.
+__host__ __device__ inline size_t vring_index(int R, int p, int c) {
+    const int r = p % R;
+    return (size_t)(r >> 2) * (kHeadDim * 4) + (size_t)c * 4 + (size_t)(r & 3);
+}
+
 // Value tokens quantised after T appends: the window keeps the R newest
 // tokens; with vflush the Values share the Key boundary R*floor(T/R).
 __host__ __device__ inline int value_boundary(const CacheView& v, int T) {

@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         uint2 vr[8];
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
-            vr[tt] = *reinterpret_cast<const uint2*>(ringV + (size_t)(16 * tt + n) * R + (pq % R));
+            vr[tt] = *reinterpret_cast<const uint2*>(ringV + vring_index(R, pq, 16 * tt + n));
         if (raw_chunk && p0 + kTile > P) {  // chunk tokens replace their ring halves (uniform test)
             bool inc[4];
             const uint16_t* vrow[4];

@@ -132,9 +132,11 @@ class PoolView:
         # residual rings
         rb = L["ring_bytes"]
         kr = self.b[L["k_ring"] + (slot * H + h) * rb: L["k_ring"] + (slot * H + h + 1) * rb].view("<u2").reshape(R, D)
-        vr = self.b[L["v_ring"] + (slot * H + h) * rb: L["v_ring"] + (slot * H + h + 1) * rb].view("<u2").reshape(D, R)
+        vr = self.b[L["v_ring"] + (slot * H + h) * rb: L["v_ring"] + (slot * H + h + 1) * rb].view("<u2")
+        vr = vr.reshape(R // 4, D, 4)  # quads of [channel][4 tokens]
         out["k_res"] = np.stack([kr[p % R] for p in range(TK, T)]) if T > TK else np.zeros((0, D), np.uint16)
-        out["v_res"] = np.stack([vr[:, p % R] for p in range(TV, T)]) if T > TV else np.zeros((0, D), np.uint16)
+        out["v_res"] = np.stack([vr[(p % R) // 4, :, p % 4] for p in range(TV, T)]) if T > TV else \
+            np.zeros((0, D), np.uint16)
         return out
 
 
@@ -204,7 +206,7 @@ def check_decode_step_state(mirror: PoolMirror, bt_np: np.ndarray, orcs: list, l
     nch = D * Bk // G
     S = len(orcs)
     ringK = b[L["k_ring"]:L["k_ring"] + gc.cfg.max_seqs * H * L["ring_bytes"]].view("<u2").reshape(-1, H, R, D)
-    ringV = b[L["v_ring"]:L["v_ring"] + gc.cfg.max_seqs * H * L["ring_bytes"]].view("<u2").reshape(-1, H, D, R)
+    ringV = b[L["v_ring"]:L["v_ring"] + gc.cfg.max_seqs * H * L["ring_bytes"]].view("<u2").reshape(-1, H, R // 4, D, 4)
 
     def page_bytes(base, per, p):
         return b[base + p * H * per: base + (p + 1) * H * per].reshape(H, per)
@@ -255,8 +257,8 @@ def check_decode_step_state(mirror: PoolMirror, bt_np: np.ndarray, orcs: list, l
         a = orcs[s].arrays()
         if T > TK and not np.array_equal(ringK[s][:, np.arange(TK, T) % R], a["k_raw"][:, TK:T]):
             raise AssertionError(f"{label}: Key residual seq {s}")
-        if T > TV and not np.array_equal(np.swapaxes(ringV[s][:, :, np.arange(TV, T) % R], 1, 2),
-                                         a["v_raw"][:, TV:T]):
+        rv = np.arange(TV, T) % R
+        if T > TV and not np.array_equal(np.swapaxes(ringV[s][:, rv // 4, :, rv % 4], 0, 1), a["v_raw"][:, TV:T]):
             raise AssertionError(f"{label}: Value residual seq {s}")
 
 
