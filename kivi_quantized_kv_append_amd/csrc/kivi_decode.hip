@@ -48,6 +48,10 @@ constexpr int kWaves = 8;
 // younger wave takes 200 minus this): measured best at 130 on MI355X.
 constexpr int kOldShare = 130;
 constexpr int kAppendShare = 70;  // main-tile share of the appending wave (20-70 measure alike)
+// Main tiles keep the 1024 offsets of the Key codes (one and-or per pair, no
+// subtract) and take 1024 sum_c Q'[n][c] out of the table's bias; the tail
+// tiles, whose tables are built apart, use exact codes.
+constexpr bool kFoldK = true;
 // Tiles per load buffer (two buffers per wave): deeper for the lighter
 // Value metadata of wide Value groups, and never more than the tiles of a
 // Key group (so at most one group begins inside a buffer).
@@ -482,12 +486,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             constexpr bool kPair = kHalf > 1;
             const bool oka = b.ok[e], okb = kPair ? b.ok[kPair ? e + 1 : e] : false;
             if (!oka && !okb) continue;
-            if ((t & (tpg - 1)) == 0 && t != m_begin) bias = build_table<BITS>(g, b.ms, b.mz, lq, lt, lbias, nr, sgn);
+            if ((t & (tpg - 1)) == 0 && t != m_begin)
+                bias = build_table<BITS, kFoldK>(g, b.ms, b.mz, lq, lt, lbias, nr, sgn);
             const TileRegs<BITS, NG>& ta = b.t[e];
             const TileRegs<BITS, NG>& tb = b.t[kPair ? e + 1 : e];
-            const f4 ra = code_scores<BITS>(ta.k, lt, lane_row, bias);
+            const f4 ra = code_scores<BITS, kFoldK>(ta.k, lt, lane_row, bias);
             f4 rb = ra;
-            if (kPair) rb = code_scores<BITS>(tb.k, lt, lane_row, bias);
+            if (kPair) rb = code_scores<BITS, kFoldK>(tb.k, lt, lane_row, bias);
             float mx = oka ? max4(ra) : -INFINITY;
             if (okb) mx = max2(mx, max4(rb));
             st.rescale(xor_max(mx), sl2, thr);
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     }
     if (m_begin < m_end) {
-        bias = build_table<BITS>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
+        bias = build_table<BITS, kFoldK>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
         int it = 0;
         for (int t0 = t_first; t0 < m_end; t0 += 2 * kHalf) {
             issue(t0 + kHalf, bb);
