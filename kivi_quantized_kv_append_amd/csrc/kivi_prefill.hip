@@ -32,6 +32,7 @@ using namespace attn;
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kRowsPerWave = 16;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 // Main-loop Key codes keep their 1024 offsets, taken out through the table's
 // bias (saves a packed subtract per code pair); the tail stays exact.
 constexpr bool kFoldK = true;
@@ -72,8 +73,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const CacheView& V = a.v;
     const int H = V.H;
-    const int wg = blockIdx.x % a.wg_per_sh;
-    const int sh = blockIdx.x / a.wg_per_sh;
+    // Work groups are dealt to the 8 XCDs in turn (block b to XCD b % 8). The
+    // blocks of one XCD take consecutive work items, so the work groups of one
+    // (sequence, KV head), which all read its cache, share that XCD's L2.
+    const int nblk = (int)gridDim.x, xcd = (int)blockIdx.x % kXcds, per = nblk / kXcds, extra = nblk % kXcds;
+    const int item = xcd * per + min(xcd, extra) + (int)blockIdx.x / kXcds;
+    const int wg = item % a.wg_per_sh;
+    const int sh = item / a.wg_per_sh;
     const int s = sh / H, h = sh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
