@@ -93,6 +93,8 @@ def lib():
             L.orc_fp8_cache_arrays.argtypes = [P, c.POINTER(P), c.POINTER(P)]
             L.orc_fp8_attention.argtypes = [P, c.c_int, c.c_int, P, c.c_int, c.c_double, P, c.c_int]
             L.orc_fp8_attention.restype = c.c_int
+            L.orc_fp8_attention_rows.argtypes = [P, c.c_int, c.c_int, P, c.c_int, P, c.c_double, c.c_int, P, c.c_int]
+            L.orc_fp8_attention_rows.restype = c.c_int
             _lib = L
     return _lib
 
@@ -375,6 +377,24 @@ def fp8_attention(caches, H_Q: int, q_bits: np.ndarray, q_dtype: int, sigma: flo
     out = np.zeros((S, H_Q, d), dtype=np.float64)
     rc = lib().orc_fp8_attention(ctypes.cast(arr, ctypes.c_void_p), S, H_Q, _ptr(q), q_dtype, float(sigma),
                                  _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad FP8 attention arguments")
+    return out
+
+
+def fp8_attention_rows(caches, H_Q: int, q_bits: np.ndarray, q_dtype: int, cu_q, sigma: float, causal: bool,
+                       threads: int = 1):
+    """Prefill over FP8 caches: q_bits [total_q][H_Q][d]; row i of request s sits at position
+    T_s - n_q,s + i and sees positions up to itself (causal) or all T_s tokens; a row that sees
+    no token is zero. Returns [total_q][H_Q][d] float64."""
+    S = len(caches)
+    arr = (ctypes.c_void_p * S)(*[c.handle for c in caches])
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+    d = caches[0].d
+    out = np.zeros((int(cu[-1]), H_Q, d), dtype=np.float64)
+    rc = lib().orc_fp8_attention_rows(ctypes.cast(arr, ctypes.c_void_p), S, H_Q, _ptr(q), q_dtype, _ptr(cu),
+                                      float(sigma), 1 if causal else 0, _ptr(out), int(threads))
     if rc != 0:
         raise ValueError("oracle: bad FP8 attention arguments")
     return out

@@ -623,6 +623,45 @@ int orc_fp8_attention(void** caches, int S, int H_Q, const uint16_t* q, int q_dt
     return 0;
 }
 
+// Prefill over FP8 caches: q [total_q][H_Q][d] raw bits, cu_q [S+1]; row i of
+// request s sits at position T_s - n_q,s + i and sees positions 0..itself
+// (causal) or all T_s tokens; a row that sees no token is zero.
+// out [total_q][H_Q][d].
+int orc_fp8_attention_rows(void** caches, int S, int H_Q, const uint16_t* q, int q_dtype, const int* cu_q,
+                           double sigma, int causal, double* out, int threads) {
+    if (S <= 0) return -1;
+    for (int s = 0; s < S; ++s)
+        if (H_Q % static_cast<const Fp8SeqCache*>(caches[s])->H) return -1;
+    const long n_items = (long)cu_q[S] * H_Q;
+    std::atomic<long> next(0);
+    auto work = [&]() {
+        for (;;) {
+            long it = next.fetch_add(1);
+            if (it >= n_items) break;
+            int r = (int)(it / H_Q), hq = (int)(it % H_Q);
+            int s = 0;
+            while (s + 1 <= S && cu_q[s + 1] <= r) ++s;
+            const Fp8SeqCache* c = static_cast<const Fp8SeqCache*>(caches[s]);
+            int d = c->d, h = hq / (H_Q / c->H);
+            int nq = cu_q[s + 1] - cu_q[s];
+            int pos = c->T - nq + (r - cu_q[s]);
+            int n = causal ? std::min(pos + 1, c->T) : c->T;
+            double* o = &out[it * d];
+            if (n <= 0) { for (int ch = 0; ch < d; ++ch) o[ch] = 0.0; continue; }
+            std::vector<float> qf(d);
+            for (int ch = 0; ch < d; ++ch) qf[ch] = load_elem(q[((size_t)r * H_Q + hq) * d + ch], q_dtype);
+            attend_tokens(d, qf.data(), n, [&](int t, int ch) { return c->k_hat(h, t, ch); },
+                          [&](int t, int ch) { return c->v_hat(h, t, ch); }, sigma, o);
+        }
+    };
+    int nt = threads > 0 ? threads : 1;
+    std::vector<std::thread> pool;
+    for (int i = 1; i < nt; ++i) pool.emplace_back(work);
+    work();
+    for (auto& th : pool) th.join();
+    return 0;
+}
+
 int orc_hardware_threads() { return (int)std::thread::hardware_concurrency(); }
 
 }  // extern "C"

@@ -156,6 +156,40 @@ def test_fp8_grid_inputs_restore_exactly():
                                    rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_rows_brute_force(causal):
+    """Prefill rows (GQA 2, two requests, one with more rows than tokens) against numpy float64
+    softmax over values restored by hand with torch's conversion; rows that see no token are zero."""
+    rng = np.random.default_rng(36)
+    H, HQ, d = 2, 4, 16
+    lens, nqs = [23, 5], [6, 7]
+    ks, vs = np.array([0.03, 0.05], np.float32), np.array([0.01, 0.02], np.float32)
+    caches, kv = [], []
+    for T in lens:
+        kb, vb = _stream(rng, T, H, d, DT_F16)
+        c = oracle.Fp8SeqCache(H, d, DT_F16, T, ks, vs, True)
+        c.append(kb, vb)
+        caches.append(c)
+        kv.append((_as_f32(kb, DT_F16), _as_f32(vb, DT_F16)))
+    cu = np.concatenate([[0], np.cumsum(nqs)])
+    qb = (rng.standard_normal((int(cu[-1]), HQ, d)) / math.sqrt(d)).astype(np.float16).view(np.uint16)
+    out = oracle.fp8_attention_rows(caches, HQ, qb, DT_F16, cu, 0.6, causal)
+    q = qb.view(np.float16).astype(np.float64)
+    for s, (T, nq) in enumerate(zip(lens, nqs)):
+        kf, vf = kv[s]
+        for i in range(nq):
+            r = cu[s] + i
+            n = min(T - nq + i + 1, T) if causal else T
+            for hq in range(HQ):
+                h = hq // 2
+                if n <= 0:
+                    assert np.all(out[r, hq] == 0)
+                    continue
+                K = (_torch_e4m3_value(_torch_e4m3(np.clip(kf[:n, h] / ks[h], -448, 448))) * ks[h]).astype(np.float32)
+                V = (_torch_e4m3_value(_torch_e4m3(np.clip(vf[:n, h] / vs[h], -448, 448))) * vs[h]).astype(np.float32)
+                np.testing.assert_allclose(out[r, hq], _numpy_attention(q[r, hq], K, V, 0.6), rtol=1e-12, atol=1e-13)
+
+
 def test_fp8_empty_sequence_row_is_zero():
     c = oracle.Fp8SeqCache(1, 16, DT_F16, 4, [1.0], [1.0], False)
     out = oracle.fp8_attention([c], 2, np.zeros((1, 2, 16), np.uint16), DT_F16, 0.25)
