@@ -302,6 +302,23 @@ kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs,
                                       const int32_t* d_block_table, int32_t bt_stride, float softmax_scale,
                                       void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* Chunked prefill attention over an FP8 cache ("4.4 KV Cache 量化", sections
+ * 2 and 4.5: values restored, value * scale, attention in fp32), after the
+ * chunk's tokens were appended with kivi_fp8_append_tokens.
+ *   d_q[total_q][H_Q][128] kv_dtype; rows of sequence s are d_cu_q[s] ..
+ *                       d_cu_q[s+1]-1 and row i sits at position
+ *                       seq_len_s - n_q,s + i
+ *   causal              1: row i attends positions 0..its own; 0: all
+ *   d_out[total_q][H_Q][128] kv_dtype (a row that sees no token gets zeros)
+ *   d_k_scale, d_v_scale as for kivi_fp8_append_tokens
+ * Other arguments as for kivi_fp8_decode_attention; no workspace.
+ * Errors: INVALID_ARG, UNSUPPORTED, DEVICE.                                   */
+kivi_status kivi_fp8_prefill_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                       const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                       const int32_t* d_seq_lens, int32_t max_seq_len, const float* d_k_scale,
+                                       const float* d_v_scale, const int32_t* d_block_table, int32_t bt_stride,
+                                       float softmax_scale, int32_t causal, void* d_out, void* stream);
+
 /* Workspace bytes kivi_prefill_attention needs (0 today; reserved).          */
 kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
                                          int32_t num_q_heads, int32_t max_q_len,

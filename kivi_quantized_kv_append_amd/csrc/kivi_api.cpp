@@ -509,6 +509,38 @@ kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs,
     return device_status(err, "FP8 decode launch");
 }
 
+kivi_status kivi_fp8_prefill_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                       const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
+                                       const int32_t* d_seq_lens, int32_t max_seq_len, const float* d_k_scale,
+                                       const float* d_v_scale, const int32_t* d_block_table, int32_t bt_stride,
+                                       float softmax_scale, int32_t causal, void* d_out, void* stream) {
+    kivi_status s = check_fp8_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0 || max_q_len < 0 || max_seq_len < 0) return fail(KIVI_ERR_INVALID_ARG, "bad sizes");
+    if (causal != 0 && causal != 1) return fail(KIVI_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (num_seqs == 0 || max_q_len == 0) return ok();
+    if (!d_q || !d_cu_q || !d_seq_lens || !d_k_scale || !d_v_scale || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_cu_q, 4) || !aligned(d_seq_lens, 4) || !aligned(d_block_table, 4) || !aligned(d_k_scale, 4) ||
+        !aligned(d_v_scale, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 or float array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const int g = num_q_heads / cache->cfg.num_kv_heads;
+    if ((int64_t)max_q_len * g > (int64_t)INT32_MAX / 2)
+        return fail(KIVI_ERR_UNSUPPORTED, "max_q_len %d too large", max_q_len);
+    int err = kivi::launch_fp8_prefill(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, num_q_heads, d_q,
+                                       d_cu_q, max_q_len, d_seq_lens, d_k_scale, d_v_scale, d_block_table, bt_stride,
+                                       softmax_scale, causal, d_out, stream);
+    return device_status(err, "FP8 prefill launch");
+}
+
 kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_seqs,
                                          int32_t num_q_heads, int32_t max_q_len,
                                          int32_t max_seq_len, size_t* bytes) {

@@ -108,6 +108,10 @@ int launch_fp8_append(const CacheView& v, int per_head, int num_seqs, const int3
                       const int32_t* cu_new, int max_new, const void* k_new, const void* v_new,
                       const float* k_scale, const float* v_scale, const int32_t* block_table, int bt_stride,
                       void* stream);
+int launch_fp8_prefill(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* cu_q, int max_q_len, const int32_t* seq_lens, const float* k_scale,
+                       const float* v_scale, const int32_t* block_table, int bt_stride, float softmax_scale,
+                       int causal, void* out, void* stream);
 int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
                       const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                       const int32_t* block_table, int bt_stride, float softmax_scale, void* out, float* partials,

@@ -523,6 +523,18 @@ class Fp8GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16)
 
+    def prefill(self, q_bits: np.ndarray, cu_q: np.ndarray, scale: float, causal=True) -> np.ndarray:
+        """kivi_fp8_prefill_attention over the cache as it stands (the chunk already appended)."""
+        torch, S, HQ = self.torch, self.w.num_seqs, self.w.num_q_heads
+        out = torch.full((max(int(cu_q[-1]), 1), HQ, D), -1, dtype=torch.int16, device=self.device)
+        mql = int(np.diff(cu_q).max())
+        kivi.kivi_fp8_prefill_attention(self.handle, S, HQ, self.t(np.ascontiguousarray(q_bits).view(np.int16)),
+                                        self.t(cu_q.astype(np.int32)), mql, self.t(self.lens.astype(np.int32)),
+                                        int(self.lens.max()), self.ks, self.vs, self.bt, self.bt.shape[1], scale,
+                                        int(causal), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)[:int(cu_q[-1])]
+
     def codes(self, s: int, h: int) -> dict:
         """The stored K and V codes of sequence s, head h: [T][128] uint8 each."""
         self.torch.cuda.synchronize()

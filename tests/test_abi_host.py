@@ -242,7 +242,8 @@ def test_each_cache_kind_takes_only_its_calls():
                      lambda: kivi.kivi_decode_step(h8, 2, 32, D, D, D, D, D, 64, D, 1, 0.1, D, D, 1 << 20),
                      lambda: kivi.kivi_prefill_attention(h8, 2, 32, D, D, 16, D, D, 64, D, 1, 0.1, 1, D),
                      lambda: kivi.kivi_fp8_append_tokens(h4, 2, D, D, 1, D, D, D, D, D, 1),
-                     lambda: kivi.kivi_fp8_decode_attention(h4, 2, 32, D, D, 64, D, D, D, 1, 0.1, D, D, 1 << 20)):
+                     lambda: kivi.kivi_fp8_decode_attention(h4, 2, 32, D, D, 64, D, D, D, 1, 0.1, D, D, 1 << 20),
+                     lambda: kivi.kivi_fp8_prefill_attention(h4, 2, 32, D, D, 16, D, 64, D, D, D, 1, 0.1, 1, D)):
             with pytest.raises(kivi.KiviError) as e:
                 call()
             assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
@@ -251,6 +252,10 @@ def test_each_cache_kind_takes_only_its_calls():
         with pytest.raises(kivi.KiviError) as e:
             kivi.kivi_fp8_append_tokens(h8, 2, D, D, 1, D, D, None, D, D, 1)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_prefill_attention(h8, 2, 32, D, D, 16, D, 64, D, D, D, 1, 0.1, 2, D)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG and "causal" in kivi.kivi_last_error()
+        kivi.kivi_fp8_prefill_attention(h8, 0, 32, None, None, 0, None, 0, None, None, None, 1, 0.1, 1, None)
         ws = kivi.kivi_decode_workspace_bytes(h8, 4, 32, 32768)
         assert ws > 0
         with pytest.raises(kivi.KiviError) as e:

@@ -85,3 +85,39 @@ def test_fp8_llama_decode_full_size():
     two heads compared, every output against the oracle."""
     w = inputs.config(2)
     _case(w, per_head=True, heads=(0, 5))
+
+
+def _fp8_prefill_case(w, per_head, chunk_lens, causal, seed=5):
+    """Append every stream (the chunk included), then prefill rows at the end of each request."""
+    ks, vs = amax_scales(w, per_head)
+    gc = Fp8GpuCache(w, ks, vs, per_head)
+    streams = [w.kv_stream(s) for s in range(w.num_seqs)]
+    gc.append([st[0] for st in streams], [st[1] for st in streams])
+    orcs = fp8_oracle_caches(w, ks, vs, per_head, lens=w.final_lens)
+    cu = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int64)
+    q = inputs.to_bits(np.random.default_rng(seed).standard_normal((int(cu[-1]), w.num_q_heads, 128)) * w.q_scale,
+                       w.dtype)
+    got = gc.prefill(q, cu, SCALE, causal=causal)
+    ref = oracle.fp8_attention_rows(orcs, w.num_q_heads, q, w.dtype, cu, SCALE, causal, threads=8)
+    return check_attention(got, ref, w.dtype, label=f"{w.name} fp8 prefill causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_ragged(causal):
+    """Chunks of 90, 17, 1 and 0 rows (GQA 3, per-head scales); the last request has 3 tokens
+    and 5 rows, so its first causal rows see nothing and are zero."""
+    w = inputs.config(1, num_seqs=4, num_kv_heads=2, num_q_heads=6, seq_lens=[150, 400, 37, 3], shuffle=True,
+                      pool_factor=1.5, block_size=32)
+    _fp8_prefill_case(w, True, [90, 17, 0, 5], causal)
+
+
+def test_fp8_prefill_qwen_shape_bf16():
+    """Qwen2.5-7B head shape (28 Q / 4 KV, GQA 7, bf16), per-tensor scales, reduced lengths."""
+    w = inputs.config(5, num_seqs=2, seq_lens=[1900, 700], extra_tokens=128, shuffle=True, pool_factor=1.3)
+    _fp8_prefill_case(w, False, [128, 128], True)
+
+
+def test_fp8_prefill_gqa16_long_chunk():
+    """GQA 16 (16 rows of one token per wave) and a chunk longer than a page window of 64 tiles."""
+    w = inputs.config(3, num_seqs=1, seq_lens=[1500], num_kv_heads=1, num_q_heads=16, extra_tokens=1100)
+    _fp8_prefill_case(w, True, [1100], True)
