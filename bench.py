@@ -399,6 +399,69 @@ def fp8_leg(torch, kivi, inputs, dev, int4_decode_us: float, check: bool, n_call
     return res
 
 
+def fp8_prefill_leg(torch, kivi, inputs, dev, n_iter: int, check: bool):
+    """Chunked prefill over an FP8 cache on the Qwen2.5-7B head shape (8 requests, 16384
+    cached tokens + a 512-token causal chunk, bf16, per-head scales max|x|/448): the whole
+    stream appended, then kivi_fp8_prefill_attention launches back to back."""
+    w = inputs.config(5)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    P, C = int(w.seq_lens[0]), int(w.extra_tokens)
+    streams = w.kv_streams()
+    km, vm = np.zeros(H), np.zeros(H)
+    for s in range(S):
+        km = np.maximum(km, np.abs(inputs.bits_to_float(streams[s][0], w.dtype)).max(axis=(0, 2)))
+        vm = np.maximum(vm, np.abs(inputs.bits_to_float(streams[s][1], w.dtype)).max(axis=(0, 2)))
+    ks, vs = (km / 448.0).astype(np.float32), (vm / 448.0).astype(np.float32)
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = kivi.make_fp8_config(H, w.block_size, w.num_blocks, 1, w.dtype, scale_per_head=1)
+    nbytes = kivi.kivi_cache_pool_bytes(cfg)
+    pool = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    h = kivi.kivi_cache_create(cfg, pool, nbytes)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    T = P + C
+    cu_all = torch.arange(0, (S + 1) * T, T, dtype=torch.int32, device=dev)
+    cu_c = torch.arange(0, (S + 1) * C, C, dtype=torch.int32, device=dev)
+    lens_t = torch.full((S,), T, dtype=torch.int32, device=dev)
+    dks, dvs = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+    kivi.kivi_fp8_append_tokens(h, S, zeros, cu_all, T, dev_u16(np.concatenate([st[0] for st in streams])),
+                                dev_u16(np.concatenate([st[1] for st in streams])), dks, dvs, bt, bt.shape[1])
+    q_bits = inputs.to_bits(np.random.default_rng(7).standard_normal((S * C, HQ, d)), w.dtype)
+    q = dev_u16(q_bits)
+    out = torch.empty((S * C, HQ, d), dtype=torch.int16, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.Stream()
+    calls = [lambda: kivi.kivi_fp8_prefill_attention(h, S, HQ, q, cu_c, C, lens_t, T, dks, dvs, bt, bt.shape[1],
+                                                     scale, 1, out, stream) for _ in range(n_iter)]
+    us = _back_to_back_us(torch, stream, calls)
+    flop = prefill_flop(P, C, HQ, S, d)
+    tflops = flop / (us * 1e-6) / 1e12
+    res = {"workload": w.name, "format": "e4m3", "scales": "per KV head, max|x|/448", "prefill_us": round(us, 1),
+           "flop_per_launch": flop,
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "kernel": "fp8_prefill_kernel, one kivi_fp8_prefill_attention call"}}
+    if check:
+        import oracle
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        k = 16  # the last k rows of request 0 (as a k-row chunk they sit at the same positions)
+        c = oracle.Fp8SeqCache(H, d, w.dtype, T, ks, vs, True)
+        c.append(streams[0][0], streams[0][1])
+        ref = oracle.fp8_attention_rows([c], HQ, q_bits[C - k:C], w.dtype, np.array([0, k]), scale, True,
+                                        threads=oracle.hardware_threads())
+        g32 = inputs.bits_to_float(got[C - k:C], w.dtype).astype(np.float64)
+        r32 = ref.astype(np.float32).astype(np.float64)
+        err = np.abs(g32 - r32)
+        res["parity"] = {"rows": f"last {k} rows of request 0, all heads", "max_abs": float(err.max()),
+                         "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
+    kivi.kivi_cache_destroy(h)
+    return res
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kivi_quantized_kv_append_amd", "csrc")
@@ -715,6 +778,9 @@ def main():
         res["ragged_stream"] = stream_leg(torch, kivi, inputs, dev)
         if args.config == 2 and args.bits == 4:
             res["fp8"] = fp8_leg(torch, kivi, inputs, dev, float(launch_ms.mean()) * 1e3, not args.no_cpu_baseline)
+            if not args.no_prefill:
+                res["fp8"]["prefill"] = fp8_prefill_leg(torch, kivi, inputs, dev, args.prefill_iters,
+                                                        not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
