@@ -179,16 +179,17 @@ struct TailRegs {
     int blk;
 };
 
-// One work group (4 waves) per (sequence, KV head, split). The main tiles
-// (Key and Value both quantised) of a (sequence, KV head) are cut into
-// 4 x n_valid contiguous wave ranges; the tail tiles (touching the residual)
-// are dealt out one per wave. Each wave streams its range on its own: page
-// ids of a 64-tile window, one buffer of tiles in flight while the other is
-// computed, and the query table of each Key group built in its own LDS rows
-// when the group begins (scales and zero-points travel with the tile loads).
-// The 4 waves merge in LDS into one partial (m, l, o) per query head; the
-// last work group of a (sequence, KV head) to finish merges the partials:
-// m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
+// One work group of kWaves waves per (sequence, KV head, split). The main
+// tiles (Key and Value both quantised) of a (sequence, KV head) are cut into
+// kWaves x n_valid contiguous wave ranges, weighted by wave age; the tail tiles
+// (touching the residual) are dealt out one per wave. Each wave streams its
+// range on its own: page ids of a 64-tile window, one buffer of tiles in
+// flight while the other is computed, and the query table of each Key group
+// built in its own LDS rows when the group begins (scales and zero-points
+// travel with the tile loads). The waves merge in LDS into the output, or,
+// when the sequence is split, into one partial (m, l, o) per query head that
+// merge_kernel combines: m = max m_i, l = sum l_i 2^(m_i - m),
+// o = sum o_i 2^(m_i - m) / l.
 template <int BITS, int DT, int NG, int kHalf>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     constexpr int TILE_BYTES = kTile * kHeadDim * BITS / 8;
