@@ -64,3 +64,12 @@ def test_fused_step_with_splits():
     kernel); only split 0 appends and reads the touched tail."""
     w = inputs.config(3, num_seqs=2, seq_lens=[5000, 8191], extra_tokens=4, shuffle=True, pool_factor=1.25)
     _run(w, 4, check_every=3)
+
+
+def test_fused_step_largest_key_group():
+    """Fused steps across a flush of a 256-token Key group (R = G = 256, 8 channels of
+    metadata per 16-token page): the flush waves quantise one whole group."""
+    w = inputs.config(1, bits=4, k_group=256, v_group=32, residual=256, num_kv_heads=2, num_q_heads=8,
+                      num_seqs=3, seq_lens=[250, 255, 511], extra_tokens=8, shuffle=True, pool_factor=1.5,
+                      n_outlier=2)
+    _run(w, 8)

@@ -193,3 +193,20 @@ def test_llama_decode_full_size():
     got = gc.decode(q, SCALE)
     ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(S + 1), SCALE, False, threads=16)
     check_attention(got, ref, w.dtype, label="llama full-size decode")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_largest_key_group_and_long_residual(bits):
+    """The largest Key group (G = 256 over 16-token pages: 8 channels of metadata per page),
+    the narrowest Value groups (Gv = 16) and a 512-token residual: single tokens and bulk
+    appends across two flushes, state compared after every call, decode after each."""
+    w = _variant(1, bits=bits, k_group=256, v_group=16, residual=512, block_size=16, num_kv_heads=2,
+                 num_q_heads=8, num_seqs=2, seq_lens=[1300, 700], shuffle=True, pool_factor=1.3, n_outlier=2)
+    _append_and_compare(w, [1, 1, 510, 1, 1, 256, 300, 1])
+
+
+def test_longest_residual_flush():
+    """The longest residual the cache takes (R = 8192, G = 256): one flush of 32 Key groups."""
+    w = _variant(1, bits=4, k_group=256, v_group=128, residual=8192, block_size=16, num_kv_heads=1,
+                 num_q_heads=4, num_seqs=1, seq_lens=[8200], pool_factor=1.1, n_outlier=2)
+    _append_and_compare(w, [8191, 1, 8], decode_every=True)
