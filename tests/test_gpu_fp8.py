@@ -121,3 +121,12 @@ def test_fp8_prefill_gqa16_long_chunk():
     """GQA 16 (16 rows of one token per wave) and a chunk longer than a page window of 64 tiles."""
     w = inputs.config(3, num_seqs=1, seq_lens=[1500], num_kv_heads=1, num_q_heads=16, extra_tokens=1100)
     _fp8_prefill_case(w, True, [1100], True)
+
+
+def test_fp8_large_pages():
+    """256-token pages (16 tiles per page) for decode and prefill, per-tensor scales."""
+    w = inputs.config(2, num_seqs=3, seq_lens=[0, 300, 4097], shuffle=True, pool_factor=1.5, block_size=256)
+    _case(w, per_head=False, plan=[257, 4000])
+    wp = inputs.config(1, num_seqs=2, num_kv_heads=2, num_q_heads=8, seq_lens=[700, 260], shuffle=True,
+                       pool_factor=1.5, block_size=256)
+    _fp8_prefill_case(wp, False, [200, 260], True)

@@ -210,3 +210,22 @@ def test_longest_residual_flush():
     w = _variant(1, bits=4, k_group=256, v_group=128, residual=8192, block_size=16, num_kv_heads=1,
                  num_q_heads=4, num_seqs=1, seq_lens=[8200], pool_factor=1.1, n_outlier=2)
     _append_and_compare(w, [8191, 1, 8], decode_every=True)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_large_pages(bits):
+    """64-token pages (four 16-token tiles per page, one Key group per page), ragged lengths,
+    shuffled pages: state after one bulk append, then decode."""
+    lens = [0, 17, 64, 191, 1000, 3001]
+    w = _variant(2, bits=bits, block_size=64, num_seqs=len(lens), seq_lens=lens, shuffle=True, pool_factor=1.3)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(w.num_seqs)])
+    gc.append(list(rk), list(rv))
+    pv = gc.pool_view()
+    for s in range(w.num_seqs):
+        compare_seq_state(pv.seq_state(gc.bt_np[s], s, int(w.seq_lens[s]), 3), orc[s], 3, label=f"seq {s}")
+    q = w.q_decode(2)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False, threads=8)
+    check_attention(got, ref, w.dtype, label="64-token pages")

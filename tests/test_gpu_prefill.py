@@ -79,3 +79,10 @@ def test_prefill_qwen_full_size_sampled():
     heads = rng.integers(0, w.num_q_heads, rows.size).astype(np.int32)
     ref = oracle.attention(orc, w.num_q_heads, q, w.dtype, cu, SCALE, True, rows, heads, threads=8)
     check_attention(got[rows, heads], ref, w.dtype, label="qwen full-size prefill (sampled)")
+
+
+def test_prefill_large_pages():
+    """64-token pages under the Qwen head shape (G = 128: a Key group spans two pages)."""
+    w = inputs.config(5, num_seqs=2, seq_lens=[900, 333], extra_tokens=100, block_size=64, shuffle=True,
+                      pool_factor=1.5)
+    _prefill_case(w, [100, 100], causal=True)
