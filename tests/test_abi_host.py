@@ -275,3 +275,12 @@ def test_each_cache_kind_takes_only_its_calls():
 def test_status_strings():
     for s in range(6):
         assert kivi.kivi_status_string(s).startswith("KIVI_")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark is one-GPU only: --gpus above 1 exits with a message, before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
