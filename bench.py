@@ -207,7 +207,7 @@ def _back_to_back_us(torch, stream, calls, runs: int = 3) -> float:
     return float(np.mean(out))
 
 
-def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 100):
+def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 100, cpu_check: bool = False):
     """kivi_decode_attention on workload cfg_id (every token already appended), launched back
     to back over replica caches that together exceed the last-level cache."""
     w = inputs.config(cfg_id, bits=bits)
@@ -252,7 +252,25 @@ def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 
     for h in handles:
         kivi.kivi_cache_destroy(h)
     gbs = nbytes / (us * 1e-6) / 1e9
+    cpu1 = None
+    if cfg_id == 1 and cpu_check:
+        # the oracle's decode of the same workload on one host thread
+        import oracle
+        caches = []
+        for s in range(S):
+            c = oracle.SeqCache(H, d, w.bits, w.k_group, w.v_group, w.residual, w.dtype, int(lens[s]))
+            c.append(streams[s][0], streams[s][1])
+            caches.append(c)
+        qh, cu_q = w.q_decode(0), np.arange(S + 1)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 0.5:
+            oracle.attention_all(caches, HQ, qh, w.dtype, cu_q, scale, False, threads=1)
+            reps += 1
+        per = (time.perf_counter() - t0) / reps
+        cpu1 = {"kind": "oracle", "cores": 1, "sample": "the whole workload, one decode call",
+                "decode_us": round(per * 1e6, 1), "value_GBs": round(nbytes / per / 1e9, 4)}
     return {"workload": w.name, "bits": bits, "num_seqs": S, "seq_len": int(lens.max()), "replicas": n_rep,
+            "cpu_baseline_1_thread": cpu1,
             "decode_us": round(us, 2), "bytes_per_call": int(nbytes),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)},
@@ -775,7 +793,9 @@ def main():
         res["prefill"] = prefill_leg(torch, kivi, inputs, dev, args.prefill_iters, not args.no_cpu_baseline)
     if not args.no_other_workloads:
         # the other workloads of the decode path, each on its own caches
-        others = [decode_leg(torch, kivi, inputs, dev, 1, 4), decode_leg(torch, kivi, inputs, dev, 1, 2)]
+        cpu_check = not args.no_cpu_baseline
+        others = [decode_leg(torch, kivi, inputs, dev, 1, 4, cpu_check=cpu_check),
+                  decode_leg(torch, kivi, inputs, dev, 1, 2, cpu_check=cpu_check)]
         if args.config != 3:
             others += [decode_leg(torch, kivi, inputs, dev, 3, 4), decode_leg(torch, kivi, inputs, dev, 3, 2)]
         res["other_workloads"] = others
