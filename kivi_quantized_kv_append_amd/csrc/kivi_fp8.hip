@@ -11,7 +11,7 @@
 // to even), stored as one byte in the lane slot layout the decode kernel
 // reads.
 //
-// Decode: one work group of 4 waves per (sequence, KV head, split); each wave
+// Decode: one work group of 8 waves per (sequence, KV head, split); each wave
 // streams a contiguous run of 16-token tiles, one buffer of kF8BufTiles tiles
 // in flight while it computes the other. An E4M3 byte becomes the fp16 number value*2^-8
 // with one byte permute and two masks (exact, subnormals included), so the
@@ -31,11 +31,13 @@ namespace {
 
 using namespace attn;
 
-constexpr int kF8Threads = 256;
+constexpr int kF8Threads = 256;  // prefill work groups: 4 waves
 constexpr int kF8Waves = 4;
+constexpr int kF8DecWaves = 8;  // decode work groups: 8 waves (4 waves measured ~4 % slower, 16 no faster)
+constexpr int kF8DecThreads = 64 * kF8DecWaves;
 constexpr int kF8TileBytes = kTile * kHeadDim;  // 2 KiB: 64 lane slots of 32 bytes
 constexpr int kF8MinSplitTiles = 32;
-constexpr int kF8ResidentGroups = 1024;  // 4-wave work groups resident at once (4 per CU)
+constexpr int kF8ResidentGroups = 512;  // 8-wave decode work groups resident at once (2 per CU)
 constexpr int kF8BufTiles = 1;  // tiles per load buffer (two buffers per wave); 2 and 4 measured slower
 
 // ---------------------------------------------------------------- append ---
@@ -142,11 +144,11 @@ struct F8Tile {
     bool ok;
 };
 
-// The second bound lets the compiler keep every value in 128 VGPRs (four
-// waves per SIMD); without it the accumulators are parked in AGPRs and copied
-// back each tile.
+// The bound of 512 threads lets the compiler keep every value in VGPRs (117:
+// two work groups per CU, four waves per SIMD); under the default bound of
+// 1024 threads the accumulators are parked in AGPRs and copied back each tile.
 template <int DT>
-__global__ __launch_bounds__(kF8Threads, 2) void fp8_decode_kernel(F8DecodeArgs a) {
+__global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int split = blockIdx.x % a.n_splits;
     const int sh = blockIdx.x / a.n_splits;
@@ -160,8 +162,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_decode_kernel(F8DecodeArgs 
     // this split's tiles, then this wave's contiguous share of them
     const int s_begin = (int)((long long)n_tiles * split / a.n_splits);
     const int s_end = (int)((long long)n_tiles * (split + 1) / a.n_splits);
-    const int w_begin = s_begin + (s_end - s_begin) * wave / kF8Waves;
-    const int w_end = s_begin + (s_end - s_begin) * (wave + 1) / kF8Waves;
+    const int w_begin = s_begin + (s_end - s_begin) * wave / kF8DecWaves;
+    const int w_end = s_begin + (s_end - s_begin) * (wave + 1) / kF8DecWaves;
 
     const float ks = a.k_scale[a.per_head ? h : 0];
     const float vs = a.v_scale[a.per_head ? h : 0];
@@ -295,9 +297,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_decode_kernel(F8DecodeArgs 
 
     // ---- merge the waves in LDS: m (log2 units), l, o per query head ----
     const float l_tot = xor_sum(l_acc);
-    float* sm_m = reinterpret_cast<float*>(smem);  // [kF8Waves][g]
-    float* sm_l = sm_m + kF8Waves * g;              // [kF8Waves][g]
-    float* sm_o = sm_l + kF8Waves * g;              // [kF8Waves][g][128]
+    float* sm_m = reinterpret_cast<float*>(smem);  // [kF8DecWaves][g]
+    float* sm_l = sm_m + kF8DecWaves * g;              // [kF8DecWaves][g]
+    float* sm_o = sm_l + kF8DecWaves * g;              // [kF8DecWaves][g][128]
     if (n < g) {
         if (j == 0) {
             sm_m[wave * g + n] = m_run;
@@ -310,14 +312,14 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_decode_kernel(F8DecodeArgs 
     }
     __syncthreads();
     const float vsc = vs * 256.0f;
-    for (int idx = tid; idx < g * kHeadDim; idx += kF8Threads) {
+    for (int idx = tid; idx < g * kHeadDim; idx += kF8DecThreads) {
         const int hn = idx / kHeadDim, chn = idx % kHeadDim;
         float mstar = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kF8Waves; ++w) mstar = fmaxf(mstar, sm_m[w * g + hn]);
+        for (int w = 0; w < kF8DecWaves; ++w) mstar = fmaxf(mstar, sm_m[w * g + hn]);
         float lsum = 0.0f, osum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kF8Waves; ++w) {
+        for (int w = 0; w < kF8DecWaves; ++w) {
             const float mw = sm_m[w * g + hn];
             const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - mstar);
             lsum += f * sm_l[w * g + hn];
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
 Fp8Plan fp8_decode_plan(int num_seqs, int num_kv_heads, int num_q_heads, int max_seq_len) {
     const int pairs = std::max(1, num_seqs * num_kv_heads);
     const int tiles = (std::max(0, max_seq_len) + kTile - 1) / kTile;
-    // about four resident 4-wave work groups per CU on 256 CUs, at least
+    // about two resident 8-wave work groups per CU on 256 CUs, at least
     // kF8MinSplitTiles tiles per split
     int n_splits = std::max(1, (kF8ResidentGroups + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (tiles + kF8MinSplitTiles - 1) / kF8MinSplitTiles));
@@ -622,9 +624,9 @@ int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_
     a.out = static_cast<uint16_t*>(out);
     hipStream_t st = static_cast<hipStream_t>(stream);
     dim3 grid((unsigned)(num_seqs * v.H * plan.n_splits));
-    const size_t lds = (size_t)kF8Waves * a.gqa * (kHeadDim + 2) * sizeof(float);
-    if (v.dtype == kF16) hipLaunchKernelGGL((fp8_decode_kernel<kF16>), grid, dim3(kF8Threads), lds, st, a);
-    else hipLaunchKernelGGL((fp8_decode_kernel<kBF16>), grid, dim3(kF8Threads), lds, st, a);
+    const size_t lds = (size_t)kF8DecWaves * a.gqa * (kHeadDim + 2) * sizeof(float);
+    if (v.dtype == kF16) hipLaunchKernelGGL((fp8_decode_kernel<kF16>), grid, dim3(kF8DecThreads), lds, st, a);
+    else hipLaunchKernelGGL((fp8_decode_kernel<kBF16>), grid, dim3(kF8DecThreads), lds, st, a);
     if (plan.n_splits > 1) {
         dim3 mgrid((unsigned)(num_seqs * num_q_heads));
         if (v.dtype == kF16)
