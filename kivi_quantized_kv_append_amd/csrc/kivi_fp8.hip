@@ -37,7 +37,9 @@ constexpr int kF8DecWaves = 8;  // decode work groups: 8 waves (4 waves measured
 constexpr int kF8DecThreads = 64 * kF8DecWaves;
 constexpr int kF8TileBytes = kTile * kHeadDim;  // 2 KiB: 64 lane slots of 32 bytes
 constexpr int kF8MinSplitTiles = 32;
-constexpr int kF8ResidentGroups = 512;  // 8-wave decode work groups resident at once (2 per CU)
+// 8-wave decode work groups launched at once: one per CU. Two per CU (twice
+// the splits, so a merge launch on the Llama-3-8B shape) measured slower.
+constexpr int kF8ResidentGroups = 256;
 constexpr int kF8BufTiles = 1;  // tiles per load buffer (two buffers per wave); 2 and 4 measured slower
 
 // ---------------------------------------------------------------- append ---
@@ -144,9 +146,9 @@ struct F8Tile {
     bool ok;
 };
 
-// The bound of 512 threads lets the compiler keep every value in VGPRs (117:
-// two work groups per CU, four waves per SIMD); under the default bound of
-// 1024 threads the accumulators are parked in AGPRs and copied back each tile.
+// The bound of 512 threads lets the compiler keep every value in VGPRs (117);
+// under the default bound of 1024 threads the accumulators are parked in
+// AGPRs and copied back each tile.
 template <int DT>
 __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
 Fp8Plan fp8_decode_plan(int num_seqs, int num_kv_heads, int num_q_heads, int max_seq_len) {
     const int pairs = std::max(1, num_seqs * num_kv_heads);
     const int tiles = (std::max(0, max_seq_len) + kTile - 1) / kTile;
-    // about two resident 8-wave work groups per CU on 256 CUs, at least
+    // about one 8-wave work group per CU on 256 CUs, at least
     // kF8MinSplitTiles tiles per split
     int n_splits = std::max(1, (kF8ResidentGroups + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (tiles + kF8MinSplitTiles - 1) / kF8MinSplitTiles));
