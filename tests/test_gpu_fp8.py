@@ -130,3 +130,40 @@ def test_fp8_large_pages():
     wp = inputs.config(1, num_seqs=2, num_kv_heads=2, num_q_heads=8, seq_lens=[700, 260], shuffle=True,
                        pool_factor=1.5, block_size=256)
     _fp8_prefill_case(wp, False, [200, 260], True)
+
+
+def test_fp8_every_code_through_decode_and_prefill():
+    """Keys and Values that are E4M3 values times power-of-two scales, so every finite code
+    (signed zeros, subnormals, +-448) is stored exactly: the stored bytes equal the codes the
+    inputs were built from, and decode and prefill over them match the oracle."""
+    grid = oracle.e4m3_to_f32(np.arange(256)).astype(np.float64)
+    finite = np.nonzero(np.isfinite(grid))[0]  # 254 codes
+    nc = len(finite)
+    T = 2 * nc
+    w = inputs.config(1, bits=4, seq_lens=[T], dtype=inputs.F16)
+    t = np.arange(T)[:, None]
+    c = np.arange(128)[None, :]
+    kc = finite[(t + c) % nc].astype(np.uint8)
+    vc = finite[(3 * t + 5 * c) % nc].astype(np.uint8)
+    ks, vs = 2.0 ** -4, 2.0 ** -6  # E4M3 values times these are fp16 numbers
+    kb = (grid[kc] * ks).astype(np.float16)[:, None, :]
+    vb = (grid[vc] * vs).astype(np.float16)[:, None, :]
+    assert np.array_equal(kb[:, 0].astype(np.float64), grid[kc] * ks)
+    assert np.array_equal(vb[:, 0].astype(np.float64), grid[vc] * vs)
+    kb, vb = kb.view(np.uint16), vb.view(np.uint16)
+    scales = np.array([ks], np.float32), np.array([vs], np.float32)
+    gc = Fp8GpuCache(w, scales[0], scales[1], False)
+    gc.append([kb[:100]], [vb[:100]])
+    gc.append([kb[100:]], [vb[100:]])
+    got = gc.codes(0, 0)
+    assert np.array_equal(got["k"], kc) and np.array_equal(got["v"], vc)
+    orc = oracle.Fp8SeqCache(1, 128, w.dtype, T, scales[0], scales[1], False)
+    orc.append(kb, vb)
+    q = w.q_decode(0)
+    check_attention(gc.decode(q, SCALE), oracle.fp8_attention([orc], w.num_q_heads, q, w.dtype, SCALE),
+                    w.dtype, label="fp8 every code decode")
+    cu = np.array([0, 40], np.int64)
+    qp = inputs.to_bits(np.random.default_rng(9).standard_normal((40, w.num_q_heads, 128)) * w.q_scale, w.dtype)
+    check_attention(gc.prefill(qp, cu, SCALE, causal=True),
+                    oracle.fp8_attention_rows([orc], w.num_q_heads, qp, w.dtype, cu, SCALE, True),
+                    w.dtype, label="fp8 every code prefill")
