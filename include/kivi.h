@@ -302,6 +302,24 @@ kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs,
                                       const int32_t* d_block_table, int32_t bt_stride, float softmax_scale,
                                       void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* One decode step on an FP8 cache: append one token per sequence (as
+ * kivi_fp8_append_tokens with one row each) and then attend with that
+ * token's query over the sequence's T + 1 tokens (as
+ * kivi_fp8_decode_attention), in two launches on the stream. The cache
+ * bytes and the outputs are those of the two calls in a row.
+ *   d_seq_lens_before[S]  tokens before this step (the query sits at position T)
+ *   d_k_new, d_v_new      [S][H_KV][128] kv_dtype, row s is sequence s's token
+ *   max_seq_len           host upper bound of d_seq_lens_before + 1 (also
+ *                         for kivi_decode_workspace_bytes)
+ * Other arguments as kivi_fp8_decode_attention. The caller guarantees a page
+ * for position d_seq_lens_before[s].
+ * Errors: INVALID_ARG, UNSUPPORTED (not an FP8 cache), WORKSPACE, DEVICE.    */
+kivi_status kivi_fp8_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads, const void* d_q,
+                                 const int32_t* d_seq_lens_before, const void* d_k_new, const void* d_v_new,
+                                 int32_t max_seq_len, const float* d_k_scale, const float* d_v_scale,
+                                 const int32_t* d_block_table, int32_t bt_stride, float softmax_scale, void* d_out,
+                                 void* d_ws, size_t ws_bytes, void* stream);
+
 /* Chunked prefill attention over an FP8 cache ("4.4 KV Cache 量化", sections
  * 2 and 4.5: values restored, value * scale, attention in fp32), after the
  * chunk's tokens were appended with kivi_fp8_append_tokens.

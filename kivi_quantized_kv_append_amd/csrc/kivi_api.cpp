@@ -509,6 +509,46 @@ kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs,
     return device_status(err, "FP8 decode launch");
 }
 
+kivi_status kivi_fp8_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads, const void* d_q,
+                                 const int32_t* d_seq_lens_before, const void* d_k_new, const void* d_v_new,
+                                 int32_t max_seq_len, const float* d_k_scale, const float* d_v_scale,
+                                 const int32_t* d_block_table, int32_t bt_stride, float softmax_scale, void* d_out,
+                                 void* d_ws, size_t ws_bytes, void* stream) {
+    kivi_status s = check_fp8_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_seq_len < 0) return fail(KIVI_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (!d_q || !d_seq_lens_before || !d_k_new || !d_v_new || !d_k_scale || !d_v_scale || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_k_new, 2) || !aligned(d_v_new, 2))
+        return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 2-byte aligned");
+    if (!aligned(d_seq_lens_before, 4) || !aligned(d_block_table, 4) || !aligned(d_k_scale, 4) ||
+        !aligned(d_v_scale, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 or float array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const kivi::Fp8Plan plan = kivi::fp8_decode_plan(num_seqs, cache->cfg.num_kv_heads, num_q_heads, max_seq_len);
+    if (plan.ws_bytes > 0 && (!d_ws || ws_bytes < plan.ws_bytes))
+        return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0, plan.ws_bytes);
+    if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // the append (one row per sequence), then the attention over T + 1 tokens
+    const kivi::CacheView view = kivi::view_of(cache);
+    int err = kivi::launch_fp8_append(view, cache->cfg.scale_per_head, num_seqs, d_seq_lens_before, nullptr, 1,
+                                      d_k_new, d_v_new, d_k_scale, d_v_scale, d_block_table, bt_stride, stream);
+    if (err != 0) return device_status(err, "FP8 decode step append launch");
+    err = kivi::launch_fp8_decode(view, cache->cfg.scale_per_head, num_seqs, num_q_heads, d_q, d_seq_lens_before,
+                                  d_k_scale, d_v_scale, d_block_table, bt_stride, softmax_scale, d_out,
+                                  static_cast<float*>(d_ws), plan, stream, 1);
+    return device_status(err, "FP8 decode step attention launch");
+}
+
 kivi_status kivi_fp8_prefill_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                        const void* d_q, const int32_t* d_cu_q, int32_t max_q_len,
                                        const int32_t* d_seq_lens, int32_t max_seq_len, const float* d_k_scale,

@@ -86,8 +86,9 @@ template <int DT>
 __global__ __launch_bounds__(kHeadDim) void fp8_append_kernel(F8AppendArgs a) {
 #pragma clang fp contract(off)
     const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
-    const int row0 = a.cu_new[s];
-    const int n = a.cu_new[s + 1] - row0;
+    // without cu_new, one row per sequence: row s (a decode step)
+    const int row0 = a.cu_new ? a.cu_new[s] : s;
+    const int n = a.cu_new ? a.cu_new[s + 1] - row0 : 1;
     const int T0 = a.seq_lens_before[s];
     if (T0 < 0) return;
     const int c = threadIdx.x;
@@ -125,6 +126,7 @@ struct F8DecodeArgs {
     const int32_t* block_table;
     int bt_stride;
     int num_q_heads, gqa, n_splits;
+    int len_add;       // tokens appended since seq_lens (1 in a decode step)
     float scale_log2;  // softmax scale * log2(e)
     float* partials;   // [S][H_Q][n_splits][kPartialStride] when n_splits > 1
     uint16_t* out;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeAr
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, j = lane >> 4;
-    const int T = max(a.seq_lens[s], 0);
+    const int T = a.seq_lens[s] < 0 ? 0 : a.seq_lens[s] + a.len_add;
     const int n_tiles = (T + kTile - 1) / kTile;
     // this split's tiles, then this wave's contiguous share of them
     const int s_begin = (int)((long long)n_tiles * split / a.n_splits);
@@ -602,7 +604,7 @@ int launch_fp8_append(const CacheView& v, int per_head, int num_seqs, const int3
 int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
                       const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                       const int32_t* block_table, int bt_stride, float softmax_scale, void* out, float* partials,
-                      const Fp8Plan& plan, void* stream) {
+                      const Fp8Plan& plan, void* stream, int len_add) {
     F8DecodeArgs a;
     a.k_codes = v.k_codes;
     a.v_codes = v.v_codes;
@@ -621,6 +623,7 @@ int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_
     a.num_q_heads = num_q_heads;
     a.gqa = num_q_heads / v.H;
     a.n_splits = plan.n_splits;
+    a.len_add = len_add;
     a.scale_log2 = softmax_scale * kLog2e;
     a.partials = partials;
     a.out = static_cast<uint16_t*>(out);

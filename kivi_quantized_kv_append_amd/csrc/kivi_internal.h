@@ -115,6 +115,6 @@ int launch_fp8_prefill(const CacheView& v, int per_head, int num_seqs, int num_q
 int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
                       const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                       const int32_t* block_table, int bt_stride, float softmax_scale, void* out, float* partials,
-                      const Fp8Plan& plan, void* stream);
+                      const Fp8Plan& plan, void* stream, int len_add = 0);
 
 }  // namespace kivi

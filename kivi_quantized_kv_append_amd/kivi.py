@@ -31,7 +31,7 @@ EXPORTED = [
     "kivi_cache_pool_bytes", "kivi_cache_capacity", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
     "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_step",
     "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_prefill_attention_raw_chunk",
-    "kivi_fp8_append_tokens", "kivi_fp8_decode_attention", "kivi_fp8_prefill_attention",
+    "kivi_fp8_append_tokens", "kivi_fp8_decode_attention", "kivi_fp8_decode_step", "kivi_fp8_prefill_attention",
     "kivi_last_error",
     "kivi_status_string",
 ]
@@ -89,6 +89,7 @@ def load():
                                                        c.c_float, I32, P, P, S, P]
         L.kivi_fp8_append_tokens.argtypes = [P, I32, P, P, I32, P, P, P, P, P, I32, P]
         L.kivi_fp8_decode_attention.argtypes = [P, I32, I32, P, P, I32, P, P, P, I32, c.c_float, P, P, S, P]
+        L.kivi_fp8_decode_step.argtypes = [P, I32, I32, P, P, P, P, I32, P, P, P, I32, c.c_float, P, P, S, P]
         L.kivi_fp8_prefill_attention.argtypes = [P, I32, I32, P, P, I32, P, I32, P, P, P, I32, c.c_float, I32, P, P]
         L.kivi_last_error.argtypes = []
         L.kivi_last_error.restype = c.c_char_p
@@ -244,6 +245,15 @@ def kivi_fp8_decode_attention(cache, num_seqs, num_q_heads, d_q, d_seq_lens, max
                                             max_seq_len, _ptr(d_k_scale), _ptr(d_v_scale), _ptr(d_block_table),
                                             bt_stride, float(softmax_scale), _ptr(d_out), _ptr(d_ws), ws_bytes,
                                             _stream(stream)))
+
+
+def kivi_fp8_decode_step(cache, num_seqs, num_q_heads, d_q, d_seq_lens_before, d_k_new, d_v_new, max_seq_len,
+                         d_k_scale, d_v_scale, d_block_table, bt_stride, softmax_scale, d_out, d_ws=None, ws_bytes=0,
+                         stream=None):
+    _check(load().kivi_fp8_decode_step(cache, num_seqs, num_q_heads, _ptr(d_q), _ptr(d_seq_lens_before),
+                                       _ptr(d_k_new), _ptr(d_v_new), max_seq_len, _ptr(d_k_scale), _ptr(d_v_scale),
+                                       _ptr(d_block_table), bt_stride, float(softmax_scale), _ptr(d_out), _ptr(d_ws),
+                                       ws_bytes, _stream(stream)))
 
 
 def kivi_fp8_prefill_attention(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_len, d_seq_lens, max_seq_len,

@@ -523,6 +523,22 @@ class Fp8GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16)
 
+    def step(self, q_bits: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float) -> np.ndarray:
+        """kivi_fp8_decode_step: row s of k_rows / v_rows ([S][H_KV][128]) is appended to
+        sequence s, then attention with q over the T + 1 tokens."""
+        torch, S, HQ = self.torch, self.w.num_seqs, self.w.num_q_heads
+        msl = int(self.lens.max()) + 1
+        ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, S, HQ, msl)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        out = torch.zeros((S, HQ, D), dtype=torch.int16, device=self.device)
+        kivi.kivi_fp8_decode_step(self.handle, S, HQ, self.t(np.ascontiguousarray(q_bits).view(np.int16)),
+                                  self.t(self.lens.astype(np.int32)), self.t(np.ascontiguousarray(k_rows).view(np.int16)),
+                                  self.t(np.ascontiguousarray(v_rows).view(np.int16)), msl, self.ks, self.vs, self.bt,
+                                  self.bt.shape[1], scale, out, ws, ws_bytes)
+        self.lens += 1
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
     def prefill(self, q_bits: np.ndarray, cu_q: np.ndarray, scale: float, causal=True) -> np.ndarray:
         """kivi_fp8_prefill_attention over the cache as it stands (the chunk already appended)."""
         torch, S, HQ = self.torch, self.w.num_seqs, self.w.num_q_heads

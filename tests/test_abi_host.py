@@ -243,6 +243,7 @@ def test_each_cache_kind_takes_only_its_calls():
                      lambda: kivi.kivi_prefill_attention(h8, 2, 32, D, D, 16, D, D, 64, D, 1, 0.1, 1, D),
                      lambda: kivi.kivi_fp8_append_tokens(h4, 2, D, D, 1, D, D, D, D, D, 1),
                      lambda: kivi.kivi_fp8_decode_attention(h4, 2, 32, D, D, 64, D, D, D, 1, 0.1, D, D, 1 << 20),
+                     lambda: kivi.kivi_fp8_decode_step(h4, 2, 32, D, D, D, D, 64, D, D, D, 1, 0.1, D, D, 1 << 20),
                      lambda: kivi.kivi_fp8_prefill_attention(h4, 2, 32, D, D, 16, D, 64, D, D, D, 1, 0.1, 1, D)):
             with pytest.raises(kivi.KiviError) as e:
                 call()
@@ -267,6 +268,20 @@ def test_each_cache_kind_takes_only_its_calls():
         with pytest.raises(kivi.KiviError) as e:
             kivi.kivi_fp8_decode_attention(h8, 4, 32, D + 8, D, 32768, D, D, D, 1, 0.1, D, D, ws)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        # the FP8 decode step: same checks, before either launch
+        kivi.kivi_fp8_decode_step(h8, 0, 32, None, None, None, None, 0, None, None, None, 1, 0.1, None)  # no-op
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_step(h8, 4, 32, D, D, D, D, 32768, D, D, D, 1, 0.1, D, D, ws - 1)
+        assert e.value.status == kivi.KIVI_ERR_WORKSPACE
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_step(h8, 4, 32, D, D, D + 1, D, 32768, D, D, D, 1, 0.1, D, D, ws)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_step(h8, 4, 32, D, D, D, D, 32768, None, D, D, 1, 0.1, D, D, ws)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_fp8_decode_step(h8, 4, 30, D, D, D, D, 32768, D, D, D, 1, 0.1, D, D, ws)
+        assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
     finally:
         kivi.kivi_cache_destroy(h8)
         kivi.kivi_cache_destroy(h4)

@@ -167,3 +167,36 @@ def test_fp8_every_code_through_decode_and_prefill():
     check_attention(gc.prefill(qp, cu, SCALE, causal=True),
                     oracle.fp8_attention_rows([orc], w.num_q_heads, qp, w.dtype, cu, SCALE, True),
                     w.dtype, label="fp8 every code prefill")
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_fp8_decode_step(per_head):
+    """kivi_fp8_decode_step (one token per request appended, then attention over T + 1): five
+    steps over lengths at tile and page edges (an empty request included), each against the
+    oracle and bit for bit against kivi_fp8_append_tokens + kivi_fp8_decode_attention on a
+    second cache; the stored codes at the end against the oracle."""
+    lens = [0, 1, 15, 16, 17, 100, 300]
+    n_steps = 5
+    w = inputs.config(1, num_seqs=len(lens), num_kv_heads=2, num_q_heads=8, seq_lens=lens, extra_tokens=n_steps,
+                      shuffle=True, pool_factor=1.5)
+    ks, vs = amax_scales(w, per_head)
+    fused, split = Fp8GpuCache(w, ks, vs, per_head), Fp8GpuCache(w, ks, vs, per_head)
+    streams = [w.kv_stream(s) for s in range(w.num_seqs)]
+    first_k = [streams[s][0][:lens[s]] for s in range(w.num_seqs)]
+    first_v = [streams[s][1][:lens[s]] for s in range(w.num_seqs)]
+    fused.append(first_k, first_v)
+    split.append(first_k, first_v)
+    orcs = fp8_oracle_caches(w, ks, vs, per_head, lens=lens)
+    for step in range(n_steps):
+        pos = [lens[s] + step for s in range(w.num_seqs)]
+        rk = np.stack([streams[s][0][pos[s]] for s in range(w.num_seqs)])
+        rv = np.stack([streams[s][1][pos[s]] for s in range(w.num_seqs)])
+        q = w.q_decode(step)
+        got = fused.step(q, rk, rv, SCALE)
+        split.append([rk[s:s + 1] for s in range(w.num_seqs)], [rv[s:s + 1] for s in range(w.num_seqs)])
+        assert np.array_equal(got, split.decode(q, SCALE)), f"step {step}: fused and two-call results differ"
+        for s, c in enumerate(orcs):
+            c.append(rk[s:s + 1], rv[s:s + 1])
+        ref = oracle.fp8_attention(orcs, w.num_q_heads, q, w.dtype, SCALE, threads=8)
+        check_attention(got, ref, w.dtype, label=f"fp8 decode step {step}")
+    _compare_codes(fused, orcs)
