@@ -207,6 +207,31 @@ def _back_to_back_us(torch, stream, calls, runs: int = 3) -> float:
     return float(np.mean(out))
 
 
+def _per_call_us(torch, stream, calls) -> dict:
+    """Duration of each call of `calls` (closures) issued back to back on `stream`,
+    with a HIP event recorded before every call and after the last: the gap between
+    two events is one call (kernel time plus the launch gap). Median, p10, p90 and
+    mean in microseconds over the calls."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    with torch.cuda.stream(stream):
+        for c in calls[:2]:
+            c()
+        torch.cuda.synchronize()
+        for i, c in enumerate(calls):
+            evs[i].record(stream)
+            c()
+        evs[-1].record(stream)
+        torch.cuda.synchronize()
+    us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(len(calls))])
+    return _dist(us)
+
+
+def _dist(us: np.ndarray) -> dict:
+    return {"n": int(us.size), "median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2), "p90_us": round(float(np.percentile(us, 90)), 2),
+            "mean_us": round(float(us.mean()), 2)}
+
+
 def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 100, cpu_check: bool = False):
     """kivi_decode_attention on workload cfg_id (every token already appended), launched back
     to back over replica caches that together exceed the last-level cache."""
@@ -249,6 +274,7 @@ def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 
         h, S, HQ, q, slots, lens_dev, msl, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
         for i in range(n_calls)]
     us = _back_to_back_us(torch, stream, calls)
+    per_call = _per_call_us(torch, stream, calls)
     for h in handles:
         kivi.kivi_cache_destroy(h)
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -271,7 +297,7 @@ def decode_leg(torch, kivi, inputs, dev, cfg_id: int, bits: int, n_calls: int = 
                 "decode_us": round(per * 1e6, 1), "value_GBs": round(nbytes / per / 1e9, 4)}
     return {"workload": w.name, "bits": bits, "num_seqs": S, "seq_len": int(lens.max()), "replicas": n_rep,
             "cpu_baseline_1_thread": cpu1,
-            "decode_us": round(us, 2), "bytes_per_call": int(nbytes),
+            "decode_us": round(us, 2), "per_call": per_call, "bytes_per_call": int(nbytes),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)},
             "kv_tokens_per_s": round(float(lens.sum()) / (us * 1e-6), 1),
@@ -313,26 +339,110 @@ def stream_leg(torch, kivi, inputs, dev, n_steps: int = 64):
     out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
     stream = torch.cuda.Stream()
     scale = 1.0 / math.sqrt(d)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         for i in range(n_steps):
+            evs[i].record(stream)
             kivi.kivi_decode_step(h, S, HQ, step_q[i], slots, lens_before[i], step_k[i], step_v[i], msl, bt,
                                   bt.shape[1], scale, out, ws, ws_bytes, stream)
-        e1.record(stream)
+        evs[-1].record(stream)
         torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n_steps
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / n_steps
+    per_step = _dist(np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_steps)]))
     kivi.kivi_cache_destroy(h)
     nbytes = float(np.mean([decode_bytes(lens + i + 1, w) for i in range(n_steps)]))
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": w.name, "num_seqs": S, "tokens_before": int(lens.sum()), "steps": n_steps,
-            "step_us": round(us, 2), "bytes_per_step": int(nbytes),
+            "step_us": round(us, 2), "per_step": per_step, "bytes_per_step": int(nbytes),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)},
             "kv_tokens_per_s": round(float(np.mean([(lens + i + 1).sum() for i in range(n_steps)])) / (us * 1e-6), 1),
             "note": "kivi_decode_step calls (append with evictions and flushes, attention) back to back, "
-                    "one HIP event pair around all steps"}
+                    "a HIP event before every step and after the last"}
+
+
+def flush_leg(torch, kivi, inputs, dev, check: bool, n_samples: int = 20, n_check: int = 4):
+    """The Llama decode layer's Key-flush step: every request holds 4222 tokens; step A
+    appends token 4222 (a Value eviction, no flush) and step B token 4223, which fills
+    the 128-token Key residual of every (request, KV head), so kivi_decode_step
+    quantises two 64-token Key groups per pair beside the attention. Each sample
+    restores the cache from a pristine copy and evicts the last-level cache with a
+    512 MB write before each timed step (one HIP event pair per step)."""
+    w = inputs.config(2, seq_lens=np.full(32, 4222), extra_tokens=2)
+    S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
+    T0 = int(w.seq_lens[0])
+    streams = w.kv_streams()
+
+    def dev_u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, w.num_blocks, S, w.dtype)
+    pool_bytes = kivi.kivi_cache_pool_bytes(cfg)
+    pristine = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    hp = kivi.kivi_cache_create(cfg, pristine, pool_bytes)
+    h = kivi.kivi_cache_create(cfg, pool, pool_bytes)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(S, dtype=torch.int32, device=dev)
+    cu = torch.arange(0, (S + 1) * T0, T0, dtype=torch.int32, device=dev)
+    dk = dev_u16(np.concatenate([streams[s][0][:T0] for s in range(S)]))
+    dv = dev_u16(np.concatenate([streams[s][1][:T0] for s in range(S)]))
+    kivi.kivi_append_tokens(hp, S, slots, zeros, cu, T0, dk, dv, bt, bt.shape[1])
+    torch.cuda.synchronize()
+    del dk, dv
+    step_k = [dev_u16(np.stack([streams[s][0][T0 + i] for s in range(S)])) for i in range(2)]
+    step_v = [dev_u16(np.stack([streams[s][1][T0 + i] for s in range(S)])) for i in range(2)]
+    step_q = [dev_u16(w.q_decode(i)) for i in range(2)]
+    lens_before = [torch.full((S,), T0 + i, dtype=torch.int32, device=dev) for i in range(2)]
+    msl = T0 + 2
+    ws_bytes = kivi.kivi_decode_workspace_bytes(h, S, HQ, msl)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(d)
+    t = {0: [], 1: []}
+    got = None
+    with torch.cuda.stream(stream):
+        for smp in range(n_samples + 1):
+            pool.copy_(pristine)
+            for i in range(2):
+                evict.fill_(smp & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                kivi.kivi_decode_step(h, S, HQ, step_q[i], slots, lens_before[i], step_k[i], step_v[i], msl, bt,
+                                      bt.shape[1], scale, out, ws, ws_bytes, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if smp > 0:  # the first sample warms up
+                    t[i].append(e0.elapsed_time(e1) * 1e3)
+            if smp == 0:
+                got = out.cpu().numpy().view(np.uint16).copy()
+    kivi.kivi_cache_destroy(h)
+    kivi.kivi_cache_destroy(hp)
+    del pool, pristine, evict
+    res = {"workload": w.name + " at T = 4222 -> 4224", "num_seqs": S,
+           "step_no_flush": _dist(np.array(t[0])) | {"bytes": decode_bytes(np.full(S, T0 + 1), w)},
+           "step_key_flush": _dist(np.array(t[1])) | {"bytes": decode_bytes(np.full(S, T0 + 2), w)},
+           "note": "kivi_decode_step on a cache restored from a pristine copy, the last-level cache evicted "
+                   "before each step; the flush step quantises 2 Key groups of 64 tokens per (request, KV head)"}
+    if check:
+        import oracle
+        caches = []
+        for s in range(n_check):
+            c = oracle.SeqCache(H, d, w.bits, w.k_group, w.v_group, w.residual, w.dtype, T0 + 2)
+            c.append(streams[s][0][:T0 + 2], streams[s][1][:T0 + 2])
+            caches.append(c)
+        ref = oracle.attention_all(caches, HQ, w.q_decode(1)[:n_check], w.dtype, np.arange(n_check + 1), scale,
+                                   False, threads=oracle.hardware_threads())
+        g32 = inputs.bits_to_float(got[:n_check], w.dtype).astype(np.float64)
+        r32 = ref.astype(np.float32).astype(np.float64)
+        err = np.abs(g32 - r32)
+        res["parity"] = {"requests": n_check, "max_abs": float(err.max()),
+                         "within_tol": bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r32)))}
+    return res
 
 
 def fp8_leg(torch, kivi, inputs, dev, int4_decode_us: float, check: bool, n_calls: int = 100):
@@ -548,12 +658,13 @@ def main():
     kivi.load()
 
     n_steps, n_warm = args.steps, args.warmup
+    n_dist = 100  # steps after the timed ones, each bracketed by HIP events (median, p10, p90)
     w0 = inputs.config(args.config, bits=args.bits)
     S, H, HQ, d = w0.num_seqs, w0.num_kv_heads, w0.num_q_heads, 128
     T0 = int(w0.seq_lens[0])
     base_bytes = decode_bytes(w0.seq_lens, w0)
     n_rep = max(1, math.ceil(2 * MALL_BYTES / base_bytes))
-    steps_per_rep = math.ceil((n_warm + n_steps) / n_rep)
+    steps_per_rep = math.ceil((n_warm + n_steps + n_dist) / n_rep)
     w = inputs.config(args.config, bits=args.bits, extra_tokens=steps_per_rep + 1)
     scale = 1.0 / math.sqrt(d)
 
@@ -589,7 +700,7 @@ def main():
     del dk, dv
 
     # per-step new tokens and queries
-    total = n_warm + n_steps
+    total = n_warm + n_steps + n_dist
     step_k, step_v, step_q = [], [], []
     for i in range(total):
         pos = T0 + i // n_rep
@@ -646,6 +757,7 @@ def main():
     stream = torch.cuda.Stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    dist_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
     step_bytes = []
 
     def one_step(i, timed_parts=False):
@@ -678,11 +790,18 @@ def main():
             one_step(i, timed_parts=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(n_warm, total):
+        for i in range(n_warm, n_warm + n_steps):
             one_step(i)
         t_issued = time.perf_counter()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        # distribution pass (after the timed steps): an event before every step
+        for k, i in enumerate(range(n_warm + n_steps, total)):
+            dist_ev[k].record(stream)
+            one_step(i)
+        dist_ev[-1].record(stream)
+        torch.cuda.synchronize()
+    step_dist = _dist(np.array([dist_ev[k].elapsed_time(dist_ev[k + 1]) * 1e3 for k in range(n_dist)]))
     wall = t1 - t0
     host_issue_us = (t_issued - t0) * 1e6 / n_steps
     part_steps = range(min(2, n_warm), n_warm)  # warm-up steps with events (first two skipped)
@@ -709,9 +828,13 @@ def main():
             torch.cuda.synchronize()
             launch_ms.append(e_a.elapsed_time(e_b) / n_dec)
     launch_ms = np.array(launch_ms)
+    launch_dist = _per_call_us(torch, stream, [
+        lambda i=i: kivi.kivi_decode_attention(handles[i % n_rep], S, HQ, step_q[i], slots, dec_lens[i % n_rep],
+                                               max_len, bt, bt.shape[1], scale, out, ws, ws_bytes, stream)
+        for i in range(n_dec)])
     launch_bytes = float(np.mean([decode_bytes(lens[i % n_rep], w) for i in range(n_dec)]))
-    timed_bytes = np.array(step_bytes[n_warm:], dtype=np.float64)
-    timed_tokens = S * np.array([T0 + 1 + i // n_rep for i in range(n_warm, total)], dtype=np.float64)
+    timed_bytes = np.array(step_bytes[n_warm:n_warm + n_steps], dtype=np.float64)
+    timed_tokens = S * np.array([T0 + 1 + i // n_rep for i in range(n_warm, n_warm + n_steps)], dtype=np.float64)
 
     ms_per_step = wall * 1e3 / n_steps
     value = float(timed_bytes.sum() / wall / 1e9)
@@ -767,8 +890,11 @@ def main():
                                   "decode": round(float(decode_ms.mean()) * 1e3, 2)} if args.separate_calls else
                                  {"decode_step": round(float(append_ms.mean()) * 1e3, 2)}) |
                                 {"note": "warm-up steps, each call bracketed by HIP events"},
+        "step_us_dist": step_dist | {"note": f"{n_dist} steps after the timed ones, a HIP event before each"},
         "decode_launch_us_mean": round(float(launch_ms.mean()) * 1e3, 2),
         "decode_launch_us_runs": [round(float(x) * 1e3, 2) for x in launch_ms],
+        "decode_launch_us_dist": launch_dist | {"note": f"{n_dec} kivi_decode_attention calls back to back, "
+                                                        "a HIP event before each"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -800,6 +926,8 @@ def main():
             others += [decode_leg(torch, kivi, inputs, dev, 3, 4), decode_leg(torch, kivi, inputs, dev, 3, 2)]
         res["other_workloads"] = others
         res["ragged_stream"] = stream_leg(torch, kivi, inputs, dev)
+        if args.config == 2 and args.bits == 4:
+            res["key_flush_step"] = flush_leg(torch, kivi, inputs, dev, not args.no_cpu_baseline)
         if args.config == 2 and args.bits == 4:
             res["fp8"] = fp8_leg(torch, kivi, inputs, dev, float(launch_ms.mean()) * 1e3, not args.no_cpu_baseline)
             if not args.no_prefill:

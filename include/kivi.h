@@ -28,11 +28,20 @@
  *     that launch work are asynchronous on that stream and return once the
  *     launches are queued.
  *   - Every argument check happens before any launch; a call that returns an
- *     error has launched nothing and changed nothing.
- *   - Ids read from device memory (slot ids, block ids) are range-checked in
- *     the kernels: a block id outside [0, num_blocks) or a slot id outside
- *     [0, max_seqs) is skipped (no memory outside the pool is touched), and
- *     the results for that sequence are unspecified.
+ *     argument or configuration error (INVALID_ARG, UNSUPPORTED,
+ *     POOL_TOO_SMALL, WORKSPACE) has launched nothing and changed nothing.
+ *     KIVI_ERR_DEVICE means a launch failed; the calls that make two
+ *     launches (kivi_fp8_decode_step, and kivi_decode_step on a v_flush
+ *     cache) may then have run the first one (the append) already.
+ *   - Values read from device memory (slot ids, page ids, lengths, row
+ *     offsets) are range-checked in the kernels in every build. One outside
+ *     its range is skipped, so no memory outside the pool, the inputs and
+ *     the outputs is touched, and the kernel sets a bit in the pool's status
+ *     word (kivi_device_error). The results for that sequence are then
+ *     unspecified; the other sequences of the call are unaffected.
+ *     kivi_check_device_errors() reports and clears the word: a serving loop
+ *     calls it when it synchronises anyway, so a bad page table fails fast
+ *     instead of serving wrong output.
  *   - Only head_dim 128 is supported (the product pages restrict their
  *     backend to head_dim 128 standard attention and fail fast otherwise);
  *     anything else is KIVI_ERR_UNSUPPORTED, never silently ignored.
@@ -56,8 +65,22 @@ typedef enum kivi_status {
     KIVI_ERR_UNSUPPORTED = 2,    /* configuration outside what the library implements */
     KIVI_ERR_POOL_TOO_SMALL = 3, /* pool_bytes below kivi_cache_pool_bytes() */
     KIVI_ERR_WORKSPACE = 4,      /* workspace missing or smaller than required */
-    KIVI_ERR_DEVICE = 5          /* a HIP call or kernel launch failed */
+    KIVI_ERR_DEVICE = 5,         /* a HIP call or kernel launch failed */
+    KIVI_ERR_DEVICE_ASSERT = 6   /* a kernel met an out-of-range id or length
+                                    (kivi_check_device_errors) */
 } kivi_status;
+
+/* Bits of the pool's status word, set by kernels that skip what they cannot
+ * use (see kivi_check_device_errors).                                       */
+typedef enum kivi_device_error {
+    KIVI_DEVERR_PAGE = 1,    /* a page-table entry outside [0, num_blocks) for a
+                                position the call reads or writes */
+    KIVI_DEVERR_SLOT = 2,    /* a residual slot id outside [0, max_seqs) */
+    KIVI_DEVERR_LENGTH = 4,  /* a negative length or row count, or a position
+                                past the page table (bt_stride pages) */
+    KIVI_DEVERR_QUERY = 8    /* a prefill query span longer than max_q_len or
+                                than its sequence */
+} kivi_device_error;
 
 typedef enum kivi_dtype {
     KIVI_F16 = 0,  /* IEEE binary16 */
@@ -119,6 +142,7 @@ typedef struct kivi_cache_config {
  *   K ring   [max_seqs][H_KV][R][128]  kv_dtype, token-major
  *   V ring   [max_seqs][H_KV][R/4][128][4]  kv_dtype: quads of 4 ring rows,
  *            channel-major inside a quad
+ *   status   256 bytes; the first 32-bit word holds kivi_device_error bits
  *
  * A token at position p of a sequence lives in page block_table[p / Bk], row
  * p % Bk; in the residual it lives in ring row r = p % R: K ring row r, V
@@ -151,8 +175,9 @@ typedef struct kivi_cache_config {
  * AND-OR per pair (the fp16 bias-exponent trick) and feed matrix cores
  * directly.
  *
- * FP8 cache (bits 8): only K codes and V codes, code_bytes = Bk*128, one
- * E4M3 byte per element; the meta and ring sub-arrays are empty. Each
+ * FP8 cache (bits 8): only K codes, V codes and the status word,
+ * code_bytes = Bk*128, one E4M3 byte per element; the meta and ring
+ * sub-arrays are empty. Each
  * 16-token sub-tile (2 KiB) is 64 lane slots of 32 bytes:
  *   K: slot L = token m, byte 8i + e holds channel 32i + 8j + e
  *      (i = 0..3, e = 0..7);
@@ -167,6 +192,7 @@ typedef struct kivi_layout {
     uint64_t k_meta_bytes;   /* per (page, head) */
     uint64_t v_meta_bytes;   /* per (page, head) */
     uint64_t ring_bytes;     /* per (slot, head), K and V alike */
+    uint64_t status;         /* offset of the 256-byte status sub-array */
 } kivi_layout;
 
 typedef struct kivi_cache kivi_cache;
@@ -193,7 +219,9 @@ kivi_status kivi_cache_capacity(const kivi_cache_config* cfg, size_t budget_byte
  * d_pool (256-byte aligned, at least kivi_cache_pool_bytes()) and frees it
  * after kivi_cache_destroy(). The handle holds host metadata only: no device
  * allocation, no device work, no synchronisation. The pool's initial
- * contents do not matter; a sequence's state is given by its length.
+ * contents do not matter; a sequence's state is given by its length. The
+ * first call that launches work on the cache also clears the status word
+ * (one small kernel on that call's stream, queued before its own kernels).
  * Errors: INVALID_ARG, UNSUPPORTED, POOL_TOO_SMALL.                          */
 kivi_status kivi_cache_create(const kivi_cache_config* cfg, void* d_pool, size_t pool_bytes,
                               kivi_cache** out);
@@ -244,6 +272,13 @@ kivi_status kivi_decode_workspace_bytes(const kivi_cache* cache, int32_t num_seq
  *   d_ws, ws_bytes      device workspace of kivi_decode_workspace_bytes()
  *                       bytes (may be NULL when that is 0)
  * H_Q must be a multiple of H_KV with H_Q/H_KV <= 16 (else UNSUPPORTED).
+ * Split plan: a long sequence's tokens may be cut over several work groups
+ * whose partial results a second kernel merges; how many depends on the
+ * whole call (num_seqs * H_KV against the device's compute units) and on
+ * max_seq_len. A sequence's output therefore may differ in its last bits
+ * (within the attention tolerance) between batches of different size or
+ * devices of different size; the same call on the same device gives the
+ * same bits every time.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
 kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                   const void* d_q, const int32_t* d_slot_ids,
@@ -348,6 +383,11 @@ kivi_status kivi_prefill_workspace_bytes(const kivi_cache* cache, int32_t num_se
  *                       d_cu_q[s+1]-1 and row i sits at position
  *                       seq_len_s - n_q,s + i
  *   causal              1: row i attends positions 0..its own; 0: all
+ *   max_q_len           host upper bound of every span d_cu_q[s+1] - d_cu_q[s];
+ *                       max_q_len * (H_Q/H_KV) must stay below 2^30
+ *                       (else UNSUPPORTED). A span longer than max_q_len or
+ *                       than its sequence sets KIVI_DEVERR_QUERY, and its
+ *                       rows are not all written
  *   d_out[total_q][H_Q][128] kv_dtype
  * Other arguments as for kivi_decode_attention.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                        */
@@ -384,6 +424,18 @@ kivi_status kivi_prefill_attention_raw_chunk(const kivi_cache* cache, int32_t nu
                                              const int32_t* d_block_table, int32_t bt_stride,
                                              float softmax_scale, int32_t causal, void* d_out, void* d_ws,
                                              size_t ws_bytes, void* stream);
+
+/* Device-side errors since the last check ("S4 KV": an unsupported input
+ * fails fast rather than giving wrong output; "给 KV cache 减肥", section 3.2:
+ * nothing the caller asked for is silently ignored). Waits for `stream`,
+ * reads the pool's status word, clears it (a small kernel queued on
+ * `stream`) and stores its kivi_device_error bits in *flags (flags may be
+ * NULL). Kernels on other streams that still run may set bits after the
+ * read; order them before the call.
+ * Returns KIVI_OK when no bit was set, KIVI_ERR_DEVICE_ASSERT (the message
+ * names the errors) when one was, INVALID_ARG, or DEVICE (a HIP call
+ * failed).                                                                  */
+kivi_status kivi_check_device_errors(const kivi_cache* cache, void* stream, uint32_t* flags);
 
 /* Message for the last failure on the calling thread ("" if none).           */
 const char* kivi_last_error(void);

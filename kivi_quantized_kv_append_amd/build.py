@@ -20,18 +20,24 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    objs = []
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel, `jobs` processes; 0 = one per source, at most
+    8) and link libkivi.so."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(HERE, "_build", os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *lang,
-               "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        cmds.append([HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *lang,
+                     "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    if verbose:
+        for cmd in cmds:
+            print(" ".join(cmd), flush=True)
+    with ThreadPoolExecutor(jobs or min(8, len(cmds))) as ex:
+        for f in [ex.submit(subprocess.check_call, cmd) for cmd in cmds]:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -1,6 +1,7 @@
 // Host side of the C ABI: configuration checks (fail fast on anything the
 // kernels do not implement), pool layout, argument checks, error reporting.
-// No device memory is allocated here and nothing waits on the device.
+// No device memory is allocated here; only kivi_check_device_errors waits on
+// the device.
 
 #include <algorithm>
 #include <cstdarg>
@@ -34,6 +35,8 @@ kivi_status ok() {
 }
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255u); }
+
+constexpr uint64_t kStatusBytes = 256;  // the status word's sub-array (one 32-bit word used)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -74,6 +77,7 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
         L.k_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
         L.v_codes = off; off += align256((uint64_t)c.num_blocks * H * L.code_bytes);
         L.k_meta = L.v_meta = L.k_ring = L.v_ring = off;
+        L.status = off;  off += kStatusBytes;
         L.total_bytes = off;
         if ((uint64_t)c.num_blocks * H * L.code_bytes >= (1ull << 32))
             return fail(KIVI_ERR_UNSUPPORTED, "code sub-array of %llu bytes exceeds 4 GiB",
@@ -117,6 +121,7 @@ kivi_status check_config(const kivi_cache_config* cfg, kivi_layout* lay) {
     L.v_meta = off;  off += align256((uint64_t)c.num_blocks * H * L.v_meta_bytes);
     L.k_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
     L.v_ring = off;  off += align256((uint64_t)c.max_seqs * H * L.ring_bytes);
+    L.status = off;  off += kStatusBytes;
     L.total_bytes = off;
     // decode addresses code pages with 32-bit offsets
     if ((uint64_t)c.num_blocks * H * L.code_bytes >= (1ull << 32))
@@ -137,6 +142,40 @@ kivi_status device_status(int err, const char* what) {
     return ok();
 }
 
+uint32_t* status_word(const kivi_cache* c) { return reinterpret_cast<uint32_t*>(c->pool + c->layout.status); }
+
+// The first call that launches work on a cache clears its status word first,
+// on the same stream (the pool's initial contents are arbitrary).
+int prepare_status(const kivi_cache* c, void* stream) {
+    if (c->status_cleared.load(std::memory_order_acquire)) return 0;
+    if (c->status_cleared.exchange(true, std::memory_order_acq_rel)) return 0;
+    const int err = kivi::launch_status_clear(status_word(c), stream);
+    if (err != 0) c->status_cleared.store(false, std::memory_order_release);
+    return err;
+}
+
+// Compute units of the current device (the decode split plan fills one round
+// of resident work groups); 256, an MI355X's count, when it cannot be read.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < 64) {
+        const int known = cache[dev].load(std::memory_order_relaxed);
+        if (known > 0) return known;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 }  // namespace
 
 namespace kivi {
@@ -150,6 +189,7 @@ CacheView view_of(const kivi_cache* c) {
     v.v_meta = c->pool + L.v_meta;
     v.k_ring = reinterpret_cast<uint16_t*>(c->pool + L.k_ring);
     v.v_ring = reinterpret_cast<uint16_t*>(c->pool + L.v_ring);
+    v.status = reinterpret_cast<uint32_t*>(c->pool + L.status);
     v.H = c->cfg.num_kv_heads;
     v.bits = c->cfg.bits;
     v.G = c->cfg.k_group;
@@ -173,9 +213,9 @@ DecodePlan decode_plan(const kivi_cache* c, int num_seqs, int num_q_heads, int m
     const int gqa = std::max(1, std::min(kMaxGqa, num_q_heads / H));
     const int main_tiles = std::max(0, max_seq_len - R) / kTile;
     const int pairs = std::max(1, num_seqs * H);
-    // one round of resident work groups (one 8-wave work group per CU on
-    // 256 CUs), at least kMinSplitTiles main tiles per split
-    const int resident = 256;
+    // one round of resident work groups (one 8-wave work group per compute
+    // unit), at least kMinSplitTiles main tiles per split
+    const int resident = device_cus();
     int n_splits = std::max(1, (resident + pairs / 2) / pairs);
     n_splits = std::min(n_splits, std::max(1, (main_tiles + kMinSplitTiles - 1) / kMinSplitTiles));
     n_splits = std::max(1, std::min(n_splits, 256));
@@ -246,6 +286,9 @@ kivi_status prefill_common(const kivi_cache* cache, int32_t num_seqs, int32_t nu
     if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
         softmax_scale == -std::numeric_limits<float>::infinity())
         return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((int64_t)max_q_len * (num_q_heads / cache->cfg.num_kv_heads) > (int64_t)INT32_MAX / 2)
+        return fail(KIVI_ERR_UNSUPPORTED, "max_q_len %d too large", max_q_len);
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_prefill(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_cu_q, max_q_len,
                                    d_slot_ids, d_seq_lens, max_seq_len, raw_chunk ? d_k_chunk : nullptr,
                                    raw_chunk ? d_v_chunk : nullptr, d_block_table, bt_stride, softmax_scale,
@@ -259,6 +302,33 @@ extern "C" {
 
 const char* kivi_last_error(void) { return g_last_error.c_str(); }
 
+kivi_status kivi_check_device_errors(const kivi_cache* cache, void* stream, uint32_t* flags) {
+    if (flags) *flags = 0;
+    kivi_status s = check_cache(cache);
+    if (s != KIVI_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!cache->status_cleared.load(std::memory_order_acquire)) {
+        // nothing has run on this cache yet: clear the word for later calls
+        if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
+        return ok();
+    }
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, status_word(cache), sizeof word, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return device_status((int)e, "status word read");
+    if (word == 0) return ok();
+    if (int err = kivi::launch_status_clear(status_word(cache), stream)) return device_status(err, "status word clear");
+    if (flags) *flags = word;
+    std::string what;
+    if (word & KIVI_DEVERR_PAGE) what += " page-table entry outside [0, num_blocks);";
+    if (word & KIVI_DEVERR_SLOT) what += " slot id outside [0, max_seqs);";
+    if (word & KIVI_DEVERR_LENGTH) what += " negative length or row count, or a position past the page table;";
+    if (word & KIVI_DEVERR_QUERY) what += " prefill query span longer than max_q_len or its sequence;";
+    if (word & ~0xFu) what += " unknown bits;";
+    return fail(KIVI_ERR_DEVICE_ASSERT, "device-side errors (0x%x):%s those sequences' results are unspecified",
+                word, what.c_str());
+}
+
 const char* kivi_status_string(kivi_status s) {
     switch (s) {
         case KIVI_OK: return "KIVI_OK";
@@ -267,6 +337,7 @@ const char* kivi_status_string(kivi_status s) {
         case KIVI_ERR_POOL_TOO_SMALL: return "KIVI_ERR_POOL_TOO_SMALL";
         case KIVI_ERR_WORKSPACE: return "KIVI_ERR_WORKSPACE";
         case KIVI_ERR_DEVICE: return "KIVI_ERR_DEVICE";
+        case KIVI_ERR_DEVICE_ASSERT: return "KIVI_ERR_DEVICE_ASSERT";
     }
     return "KIVI_ERR_UNKNOWN";
 }
@@ -354,6 +425,7 @@ kivi_status kivi_append_tokens(kivi_cache* cache, int32_t num_seqs, const int32_
     if (!aligned(d_k_new, 16) || !aligned(d_v_new, 16))
         return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
     if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_append(kivi::view_of(cache), num_seqs, d_slot_ids, d_seq_lens_before,
                                   d_cu_new, max_new, d_k_new, d_v_new, d_block_table, bt_stride,
                                   stream);
@@ -402,6 +474,7 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0,
                     plan.ws_bytes);
     if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_decode(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_slot_ids,
                                   d_seq_lens, d_block_table, bt_stride, softmax_scale, d_out,
                                   static_cast<float*>(d_ws), plan, stream);
@@ -435,6 +508,7 @@ kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0,
                     plan.ws_bytes);
     if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     const kivi::CacheView view = kivi::view_of(cache);
     if (view.vflush) {
         // Values flush with the Keys: a flush step quantises R Value tokens,
@@ -471,6 +545,7 @@ kivi_status kivi_fp8_append_tokens(kivi_cache* cache, int32_t num_seqs, const in
     if (!aligned(d_k_new, 2) || !aligned(d_v_new, 2))
         return fail(KIVI_ERR_INVALID_ARG, "k_new / v_new must be 2-byte aligned");
     if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_fp8_append(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, d_seq_lens_before,
                                       d_cu_new, max_new, d_k_new, d_v_new, d_k_scale, d_v_scale, d_block_table,
                                       bt_stride, stream);
@@ -503,6 +578,7 @@ kivi_status kivi_fp8_decode_attention(const kivi_cache* cache, int32_t num_seqs,
     if (plan.ws_bytes > 0 && (!d_ws || ws_bytes < plan.ws_bytes))
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0, plan.ws_bytes);
     if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_fp8_decode(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, num_q_heads, d_q,
                                       d_seq_lens, d_k_scale, d_v_scale, d_block_table, bt_stride, softmax_scale,
                                       d_out, static_cast<float*>(d_ws), plan, stream);
@@ -538,6 +614,7 @@ kivi_status kivi_fp8_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t nu
     if (plan.ws_bytes > 0 && (!d_ws || ws_bytes < plan.ws_bytes))
         return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", d_ws ? ws_bytes : 0, plan.ws_bytes);
     if (d_ws && !aligned(d_ws, 16)) return fail(KIVI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     // the append (one row per sequence), then the attention over T + 1 tokens
     const kivi::CacheView view = kivi::view_of(cache);
     int err = kivi::launch_fp8_append(view, cache->cfg.scale_per_head, num_seqs, d_seq_lens_before, nullptr, 1,
@@ -575,6 +652,7 @@ kivi_status kivi_fp8_prefill_attention(const kivi_cache* cache, int32_t num_seqs
     const int g = num_q_heads / cache->cfg.num_kv_heads;
     if ((int64_t)max_q_len * g > (int64_t)INT32_MAX / 2)
         return fail(KIVI_ERR_UNSUPPORTED, "max_q_len %d too large", max_q_len);
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
     int err = kivi::launch_fp8_prefill(kivi::view_of(cache), cache->cfg.scale_per_head, num_seqs, num_q_heads, d_q,
                                        d_cu_q, max_q_len, d_seq_lens, d_k_scale, d_v_scale, d_block_table, bt_stride,
                                        softmax_scale, causal, d_out, stream);

@@ -22,7 +22,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     append_body<BITS, DT, kAppendThreads>(a, s, h, row0, n, threadIdx.x, blockIdx.y, gridDim.y, sm);
 }
 
+__global__ __launch_bounds__(64) void status_clear_kernel(uint32_t* status) {
+    if (threadIdx.x == 0) status[0] = 0u;
+}
+
 }  // namespace
+
+int launch_status_clear(uint32_t* status, void* stream) {
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), status);
+    return (int)hipGetLastError();
+}
 
 int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
                   const int32_t* seq_lens_before, const int32_t* cu_new, int max_new,

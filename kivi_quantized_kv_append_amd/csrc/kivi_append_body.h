@@ -67,7 +67,13 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
 
     const int slot = a.slot_ids[s];
     const int T0 = a.seq_lens_before[s];
-    if (slot < 0 || slot >= V.max_seqs || T0 < 0 || n <= 0) return;
+    if (n == 0) return;
+    if (slot < 0 || slot >= V.max_seqs || T0 < 0 || n < 0) {  // skipped, and reported
+        if (tid == 0)
+            report_error(V.status, (slot < 0 || slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) |
+                                       (T0 < 0 || n < 0 ? KIVI_DEVERR_LENGTH : 0u));
+        return;
+    }
     const int T1 = T0 + n;
     const int R = V.R, G = V.G, Gv = V.Gv, Bk = V.Bk;
     const int TK0 = R * (T0 / R), TK1 = R * (T1 / R);
@@ -81,11 +87,17 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
     const uint16_t* inK = a.k_new + (size_t)row0 * in_stride + (size_t)h * kHeadDim;
     const uint16_t* inV = a.v_new + (size_t)row0 * in_stride + (size_t)h * kHeadDim;
 
+    // page of position p, or -1 (reported) when the table has none for it
     auto page_of = [&](int p) -> int {
         int bi = p / Bk;
-        if (bi >= bt_len) return -1;
+        if (bi >= bt_len) {
+            report_error(V.status, KIVI_DEVERR_LENGTH);
+            return -1;
+        }
         int blk = bt[bi];
-        return (blk >= 0 && blk < V.num_blocks) ? blk : -1;
+        if (blk >= 0 && blk < V.num_blocks) return blk;
+        report_error(V.status, KIVI_DEVERR_PAGE);
+        return -1;
     };
     auto kval = [&](int p, int c) -> float {
         uint16_t u = p < T0 ? ringK[(size_t)(p % R) * kHeadDim + c] : inK[(size_t)(p - T0) * in_stride + c];
@@ -336,11 +348,17 @@ struct TokenAppend {
     const uint16_t* inK;
     const uint16_t* inV;
     bool ok;
+    // page of position p, or -1 (reported) when the table has none for it
     __device__ int page_of(int p) const {
         const int bi = p / Bk;
-        if (bi >= bt_len) return -1;
+        if (bi >= bt_len) {
+            report_error(V->status, KIVI_DEVERR_LENGTH);
+            return -1;
+        }
         const int blk = bt[bi];
-        return (blk >= 0 && blk < V->num_blocks) ? blk : -1;
+        if (blk >= 0 && blk < V->num_blocks) return blk;
+        report_error(V->status, KIVI_DEVERR_PAGE);
+        return -1;
     }
 };
 

@@ -96,6 +96,7 @@ struct WgCtx {
     int s, h, g, T, TK, TV, n_main, slot;
     const int32_t* bt;
     int bt_len;
+    uint32_t err;  // kivi_device_error bits of the sequence's slot and length
 };
 
 __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
@@ -107,7 +108,9 @@ __device__ __forceinline__ WgCtx make_ctx(const DecodeArgs& a, int s, int h) {
     const int T_in = a.seq_lens[s];
     int T = T_in + a.fuse + a.len_add;
     c.slot = a.slot_ids[s];
-    if (c.slot < 0 || c.slot >= V.max_seqs || T_in < 0) T = 0;
+    c.err = (c.slot < 0 || c.slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) | (T_in < 0 ? KIVI_DEVERR_LENGTH : 0u);
+    if (c.err) T = 0;  // the sequence is skipped
+    else if ((long long)T > (long long)a.bt_stride * V.Bk) c.err = KIVI_DEVERR_LENGTH;  // past the page table
     c.T = T;
     c.TK = V.R * (T / V.R);
     c.TV = value_boundary(V, T);
@@ -204,6 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // at least kMinSplitTiles main tiles per split when there are that many
     const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
     const int tid = threadIdx.x, lane = tid & 63;
+    // device-side errors this wave met (wave-uniform), reported once at the end
+    uint32_t err = split == 0 && tid < 64 ? c.err : 0u;
     if (split >= nvalid) {  // no work: an empty partial for the merge
         if (tid < c.g)
             a.partials[(((size_t)c.s * a.num_q_heads + c.h * c.g + tid) * a.n_splits + split) * kPartialStride] =
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     auto tail_issue = [&](int t, int tpage, TailRegs<BITS, NG>& x) {
         const int tb = (t >> a.tpg_shift) << a.tpg_shift;
         x.blk = valid_page(a, __builtin_amdgcn_readlane(tpage, t - tb));
+        if (x.blk < 0) err |= KIVI_DEVERR_PAGE;  // every tail tile holds a token < T
         const int blk = max(x.blk, 0);
         const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)c.h;
         const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
@@ -446,7 +452,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < kHalf; ++e) {
             const int t = t0 + e;
             const int blk = valid_page(a, __builtin_amdgcn_readlane(my_page, (t - base) & 63));
-            b.ok[e] = blk >= 0 && t >= m_begin && t < m_end;
+            const bool mine = t >= m_begin && t < m_end;
+            b.ok[e] = blk >= 0 && mine;
+            if (blk < 0 && mine) err |= KIVI_DEVERR_PAGE;
             const uint32_t chk = (uint32_t)(b.ok[e] ? blk : 0) * (uint32_t)H + (uint32_t)c.h;
             const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
             const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
@@ -618,6 +626,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         __syncthreads();
     }
+    if (err != 0 && lane == 0) report_error(V.status, err);
     const float* sm_m = reinterpret_cast<const float*>(smem);
     const float* sm_l = sm_m + kWaves * g;
     const float* sm_o = sm_l + kWaves * g;

@@ -66,6 +66,12 @@ __device__ __forceinline__ uint32_t group_code(float x, float S, float Z, int qm
     return (uint32_t)r;
 }
 
+// Report device-side argument errors: OR kivi_device_error bits into the
+// pool's status word with a vector atomic (the lanes that call it).
+__device__ __forceinline__ void report_error(uint32_t* status, uint32_t bits) {
+    __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Min / max over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_min(float x, int width) {
     for (int o = 1; o < width; o <<= 1) x = fminf(x, __shfl_xor(x, o, 64));

@@ -70,6 +70,7 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
 struct F8AppendArgs {
     uint8_t* k_codes;
     uint8_t* v_codes;
+    uint32_t* status;  // kivi_device_error bits
     int H, Bk, num_blocks, per_head;
     uint32_t code_bytes;
     const int32_t* seq_lens_before;
@@ -90,16 +91,25 @@ __global__ __launch_bounds__(kHeadDim) void fp8_append_kernel(F8AppendArgs a) {
     const int row0 = a.cu_new ? a.cu_new[s] : s;
     const int n = a.cu_new ? a.cu_new[s + 1] - row0 : 1;
     const int T0 = a.seq_lens_before[s];
-    if (T0 < 0) return;
+    if (T0 < 0 || n < 0) {  // skipped, and reported
+        if (threadIdx.x == 0 && blockIdx.y == 0) report_error(a.status, KIVI_DEVERR_LENGTH);
+        return;
+    }
     const int c = threadIdx.x;
     const float ks = a.k_scale[a.per_head ? h : 0];
     const float vs = a.v_scale[a.per_head ? h : 0];
     for (int i = blockIdx.y; i < n; i += gridDim.y) {  // rows of the sequence's new tokens
         const int p = T0 + i;
         const int bi = p / a.Bk;
-        if (bi >= a.bt_stride) break;
+        if (bi >= a.bt_stride) {
+            if (c == 0) report_error(a.status, KIVI_DEVERR_LENGTH);
+            break;
+        }
         const int blk = a.block_table[(size_t)s * a.bt_stride + bi];
-        if (blk < 0 || blk >= a.num_blocks) continue;
+        if (blk < 0 || blk >= a.num_blocks) {
+            if (c == 0) report_error(a.status, KIVI_DEVERR_PAGE);
+            continue;
+        }
         const size_t src = ((size_t)(row0 + i) * a.H + h) * kHeadDim + c;
         const uint32_t ck = e4m3_code(to_f32<DT>(a.k_new[src]) / ks);
         const uint32_t cv = e4m3_code(to_f32<DT>(a.v_new[src]) / vs);
@@ -117,6 +127,7 @@ __global__ __launch_bounds__(kHeadDim) void fp8_append_kernel(F8AppendArgs a) {
 struct F8DecodeArgs {
     const uint8_t* k_codes;
     const uint8_t* v_codes;
+    uint32_t* status;  // kivi_device_error bits
     int H, Bk, num_blocks, per_head;
     uint32_t code_bytes, code_array_bytes;
     const uint16_t* q;
@@ -163,6 +174,11 @@ __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeAr
     const int n = lane & 15, j = lane >> 4;
     const int T = a.seq_lens[s] < 0 ? 0 : a.seq_lens[s] + a.len_add;
     const int n_tiles = (T + kTile - 1) / kTile;
+    // device-side errors this wave met (wave-uniform), reported once at the end
+    uint32_t err = 0;
+    if (split == 0 && tid < 64 &&
+        (a.seq_lens[s] < 0 || (long long)T > (long long)a.bt_stride * a.Bk))
+        err = KIVI_DEVERR_LENGTH;
     // this split's tiles, then this wave's contiguous share of them
     const int s_begin = (int)((long long)n_tiles * split / a.n_splits);
     const int s_end = (int)((long long)n_tiles * (split + 1) / a.n_splits);
@@ -218,6 +234,7 @@ __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeAr
         }
         const int pg = __builtin_amdgcn_readlane(my_page, (t - base) & 63);
         x.ok = t < w_end && pg >= 0 && pg < a.num_blocks;
+        if (t < w_end && !x.ok) err |= KIVI_DEVERR_PAGE;
         const uint32_t off = ((uint32_t)(x.ok ? pg : 0) * (uint32_t)a.H + (uint32_t)h) * a.code_bytes +
                              (uint32_t)(t & ((1 << tpp_shift) - 1)) * kF8TileBytes;
         x.k[0] = buf_b128(rk, lane_off, off);
@@ -315,6 +332,7 @@ __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeAr
             for (int r = 0; r < 4; ++r) sm_o[(wave * g + n) * kHeadDim + 16 * tt + 4 * j + r] = O[tt][r];
     }
     __syncthreads();
+    if (err != 0 && lane == 0) report_error(a.status, err);
     const float vsc = vs * 256.0f;
     for (int idx = tid; idx < g * kHeadDim; idx += kF8DecThreads) {
         const int hn = idx / kHeadDim, chn = idx % kHeadDim;
@@ -379,6 +397,8 @@ constexpr int kF8Rows = 16;  // rows per wave
 struct F8PrefillArgs {
     const uint8_t* k_codes;
     const uint8_t* v_codes;
+    uint32_t* status;  // kivi_device_error bits
+    int max_q_len;     // the caller's bound of every query span
     int H, Bk, num_blocks, per_head;
     uint32_t code_bytes, code_array_bytes;
     const uint16_t* q;
@@ -409,8 +429,14 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
     const int n = lane & 15, j = lane >> 4;
     const int q0 = a.cu_q[s], nq = a.cu_q[s + 1] - q0;
     const int T = max(a.seq_lens[s], 0);
+    if (wg == 0 && wave == 0) {  // the sequence's lengths, checked once
+        uint32_t e = a.seq_lens[s] < 0 || (long long)T > (long long)a.bt_stride * a.Bk ? KIVI_DEVERR_LENGTH : 0u;
+        if (nq < 0 || nq > a.max_q_len || nq > T) e |= KIVI_DEVERR_QUERY;
+        if (e != 0 && lane == 0) report_error(a.status, e);
+    }
     const int row0 = (wg * kF8Waves + wave) * kF8Rows;
     if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave (uniform)
+    uint32_t err = 0;  // pages this wave could not read (wave-uniform)
     // this lane's row (one of 16 per wave; the 4 lanes n, n+16, ... share it)
     const int row = row0 + n;
     const bool row_ok = row < nq * g;
@@ -471,6 +497,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
         }
         const int pg = __builtin_amdgcn_readlane(my_page, (t - base) & 63);
         x.ok = t < n_tiles && pg >= 0 && pg < a.num_blocks;
+        if (t < n_tiles && !x.ok) err |= KIVI_DEVERR_PAGE;
         const uint32_t off = ((uint32_t)(x.ok ? pg : 0) * (uint32_t)a.H + (uint32_t)h) * a.code_bytes +
                              (uint32_t)(t & ((1 << tpp_shift) - 1)) * kF8TileBytes;
         x.k[0] = buf_b128(rk, lane_off, off);
@@ -547,6 +574,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
 
     // the row's output: lane (n, j) holds channels 16 tt + 4 j + r
     const float l_tot = xor_sum(l_acc);
+    if (err != 0 && lane == 0) report_error(a.status, err);
     if (!row_ok) return;
     const float f = l_tot > 0.0f ? vs * 256.0f / l_tot : 0.0f;
     uint16_t* orow = a.out + ((size_t)(q0 + qi) * HQ + h * g + hh) * kHeadDim + 4 * j;
@@ -581,6 +609,7 @@ int launch_fp8_append(const CacheView& v, int per_head, int num_seqs, const int3
     F8AppendArgs a;
     a.k_codes = v.k_codes;
     a.v_codes = v.v_codes;
+    a.status = v.status;
     a.H = v.H;
     a.Bk = v.Bk;
     a.num_blocks = v.num_blocks;
@@ -608,6 +637,7 @@ int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_
     F8DecodeArgs a;
     a.k_codes = v.k_codes;
     a.v_codes = v.v_codes;
+    a.status = v.status;
     a.H = v.H;
     a.Bk = v.Bk;
     a.num_blocks = v.num_blocks;
@@ -655,6 +685,8 @@ int launch_fp8_prefill(const CacheView& v, int per_head, int num_seqs, int num_q
     F8PrefillArgs a;
     a.k_codes = v.k_codes;
     a.v_codes = v.v_codes;
+    a.status = v.status;
+    a.max_q_len = max_q_len;
     a.H = v.H;
     a.Bk = v.Bk;
     a.num_blocks = v.num_blocks;

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host API and the kernel launchers.
 #pragma once
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 
@@ -12,6 +13,9 @@ struct kivi_cache {
     kivi_cache_config cfg;
     kivi_layout layout;
     uint8_t* pool;   // caller-owned device memory
+    // set once the first launching call has queued the clear of the pool's
+    // status word (the pool's initial contents are arbitrary)
+    mutable std::atomic<bool> status_cleared{false};
 };
 
 namespace kivi {
@@ -28,6 +32,7 @@ struct CacheView {
     uint8_t* v_meta;
     uint16_t* k_ring;
     uint16_t* v_ring;
+    uint32_t* status;  // kivi_device_error bits, set with vector atomics
     int H, bits, G, Gv, R, Bk, num_blocks, max_seqs, dtype;
     int code_bytes, k_meta_bytes, v_meta_bytes, ring_elems;
     int vflush;  // 0: sliding Value window; 1: Values flush with the Keys
@@ -71,6 +76,9 @@ inline int append_parts(int max_new) {
     const int p = (max_new + 63) / 64;
     return p < 1 ? 1 : (p > 64 ? 64 : p);
 }
+
+// Zero the status word (one thread of one work group), on `stream`.
+int launch_status_clear(uint32_t* status, void* stream);
 
 // Kernel launchers (return a hipError_t as int).
 int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,

@@ -51,6 +51,7 @@ struct PrefillArgs {
     int gqa;
     float scale_log2;
     int causal;
+    int max_q_len;   // the caller's bound of every query span
     int wg_per_sh;   // work groups per (sequence, KV head)
     int tpg_shift;   // log2(tiles per Key group)
     int tpp_shift;   // log2(tiles per page)
@@ -94,8 +95,18 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     int P = a.seq_lens[s];
     const int slot = a.slot_ids[s];
     const bool bad = slot < 0 || slot >= V.max_seqs || P < 0;
-    if (bad) P = 0;
     const bool raw_chunk = a.k_chunk != nullptr;
+    // device-side errors this wave met (wave-uniform), reported before the output
+    uint32_t err = 0;
+    if (wg == 0 && wave == 0) {
+        err = (slot < 0 || slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) | (P < 0 ? KIVI_DEVERR_LENGTH : 0u);
+        if (nq < 0 || nq > a.max_q_len || (!raw_chunk && !bad && nq > P)) err |= KIVI_DEVERR_QUERY;
+        if (!bad && (long long)P + (raw_chunk ? max(nq, 0) : 0) > (long long)a.bt_stride * V.Bk)
+            err |= KIVI_DEVERR_LENGTH;
+        if (err != 0 && lane == 0) report_error(V.status, err);
+        err = 0;
+    }
+    if (bad) P = 0;
     const int T = bad ? 0 : P + (raw_chunk ? nq : 0);  // tokens the rows attend over
     const int row0 = (wg * kPWaves + wave) * kRowsPerWave;
     if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave
@@ -204,6 +215,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             const int t = t0 + e;
             const int blk = valid_pg(__builtin_amdgcn_readlane(my_page, (t - base) & 63));
             b.ok[e] = blk >= 0 && t < m_end;
+            if (blk < 0 && t < m_end) err |= KIVI_DEVERR_PAGE;
             const uint32_t chk = (uint32_t)(b.ok[e] ? blk : 0) * (uint32_t)H + (uint32_t)h;
             const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
             const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
@@ -309,7 +321,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int tpage = page_of(tb0 + lane);
         const int blk = valid_pg(__builtin_amdgcn_readlane(tpage, t - tb0));
         const int p0 = t * kTile, pq = p0 + 4 * j;
-        if (blk < 0 && (t < tk_tiles || p0 < TV)) continue;  // codes without a page
+        if (blk < 0 && (t < tk_tiles || p0 < TV)) {  // codes without a page
+            err |= KIVI_DEVERR_PAGE;
+            continue;
+        }
         const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)h;
         const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
         const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
@@ -438,6 +453,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - (BITS == 4 ? 1024.0f * xor_sum(st.wsum[gg][vb]) : 0.0f);
     }
+    if (err != 0 && lane == 0) report_error(V.status, err);
     if (!(row < nq * g)) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     uint16_t* orow = a.out + ((size_t)(q0 + qi) * HQ + h * g + qh) * kHeadDim;
@@ -496,6 +512,7 @@ int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void
     a.gqa = num_q_heads / v.H;
     a.scale_log2 = softmax_scale * kLog2e;
     a.causal = causal;
+    a.max_q_len = max_q_len;
     const int rows = max_q_len * a.gqa;
     const int wave_tiles = (rows + kRowsPerWave - 1) / kRowsPerWave;
     a.wg_per_sh = (wave_tiles + kPWaves - 1) / kPWaves;

@@ -23,6 +23,12 @@ KIVI_ERR_UNSUPPORTED = 2
 KIVI_ERR_POOL_TOO_SMALL = 3
 KIVI_ERR_WORKSPACE = 4
 KIVI_ERR_DEVICE = 5
+KIVI_ERR_DEVICE_ASSERT = 6
+
+KIVI_DEVERR_PAGE = 1
+KIVI_DEVERR_SLOT = 2
+KIVI_DEVERR_LENGTH = 4
+KIVI_DEVERR_QUERY = 8
 
 KIVI_F16 = 0
 KIVI_BF16 = 1
@@ -32,7 +38,7 @@ EXPORTED = [
     "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_step",
     "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_prefill_attention_raw_chunk",
     "kivi_fp8_append_tokens", "kivi_fp8_decode_attention", "kivi_fp8_decode_step", "kivi_fp8_prefill_attention",
-    "kivi_last_error",
+    "kivi_check_device_errors", "kivi_last_error",
     "kivi_status_string",
 ]
 
@@ -52,7 +58,7 @@ class kivi_cache_config(ctypes.Structure):
 class kivi_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "total_bytes",
-        "code_bytes", "k_meta_bytes", "v_meta_bytes", "ring_bytes")]
+        "code_bytes", "k_meta_bytes", "v_meta_bytes", "ring_bytes", "status")]
 
 
 _lock = threading.Lock()
@@ -91,6 +97,7 @@ def load():
         L.kivi_fp8_decode_attention.argtypes = [P, I32, I32, P, P, I32, P, P, P, I32, c.c_float, P, P, S, P]
         L.kivi_fp8_decode_step.argtypes = [P, I32, I32, P, P, P, P, I32, P, P, P, I32, c.c_float, P, P, S, P]
         L.kivi_fp8_prefill_attention.argtypes = [P, I32, I32, P, P, I32, P, I32, P, P, P, I32, c.c_float, I32, P, P]
+        L.kivi_check_device_errors.argtypes = [P, P, c.POINTER(c.c_uint32)]
         L.kivi_last_error.argtypes = []
         L.kivi_last_error.restype = c.c_char_p
         L.kivi_status_string.argtypes = [c.c_int]
@@ -263,6 +270,19 @@ def kivi_fp8_prefill_attention(cache, num_seqs, num_q_heads, d_q, d_cu_q, max_q_
                                              _ptr(d_seq_lens), max_seq_len, _ptr(d_k_scale), _ptr(d_v_scale),
                                              _ptr(d_block_table), bt_stride, float(softmax_scale), int(causal),
                                              _ptr(d_out), _stream(stream)))
+
+
+def kivi_check_device_errors(cache, stream=None) -> int:
+    """The status word's kivi_device_error bits (0 when none was set; the word is
+    cleared). Raises KiviError (KIVI_ERR_DEVICE_ASSERT) when a bit was set; the
+    exception carries the bits as ``flags``."""
+    flags = ctypes.c_uint32()
+    st = load().kivi_check_device_errors(cache, _stream(stream), ctypes.byref(flags))
+    if st != KIVI_OK:
+        e = KiviError(st, load().kivi_last_error().decode())
+        e.flags = flags.value
+        raise e
+    return flags.value
 
 
 def kivi_last_error() -> str:

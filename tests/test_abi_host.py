@@ -40,7 +40,8 @@ def test_pool_bytes_matches_layout_formula():
     kmeta = NB * H * 4 * 128 * Bk // G
     vmeta = NB * H * Bk * 1 * 4
     ring = S * H * R * 128 * 2
-    assert n == 2 * codes + kmeta + vmeta + 2 * ring
+    status = 256  # the status word's sub-array (device-side error bits)
+    assert n == 2 * codes + kmeta + vmeta + 2 * ring + status
 
 
 @pytest.mark.parametrize("bits,budget", [(4, 1 << 30), (2, 1 << 30), (4, 70 << 30), (4, 3 << 20), (4, 1000)])
@@ -201,18 +202,18 @@ def test_fp8_config_and_layout():
     M_KV formula at 8 bits."""
     c = kivi.make_fp8_config(8, 16, 2048, scale_per_head=1)
     n = kivi.kivi_cache_pool_bytes(c)
-    assert n == 2 * 2048 * 8 * 16 * 128
-    assert n == oracle.m_kv_bytes(1, 1, 2048 * 16, 8, 128, 8)
+    assert n == 2 * 2048 * 8 * 16 * 128 + 256  # codes and the status word
+    assert n - 256 == oracle.m_kv_bytes(1, 1, 2048 * 16, 8, 128, 8)
     h = kivi.kivi_cache_create(c, 1 << 20, n)
     try:
         lay = kivi.kivi_cache_layout(h)
         assert lay["code_bytes"] == 16 * 128 and lay["total_bytes"] == n
-        assert lay["k_meta"] == lay["v_meta"] == lay["k_ring"] == lay["v_ring"] == n
+        assert lay["k_meta"] == lay["v_meta"] == lay["k_ring"] == lay["v_ring"] == lay["status"] == n - 256
     finally:
         kivi.kivi_cache_destroy(h)
     # density of a 1 GiB budget against fp16 K/V: exactly 2x
     nb, tokens = kivi.kivi_cache_capacity(kivi.make_fp8_config(8, 16, 1), 1 << 30)
-    assert tokens == (1 << 30) // (2 * 8 * 128)
+    assert tokens == ((1 << 30) - 256) // (2 * 8 * 128 * 16) * 16
 
 
 @pytest.mark.parametrize("over", [dict(k_group=64), dict(v_group=128), dict(residual=128), dict(v_flush=1),
@@ -288,8 +289,24 @@ def test_each_cache_kind_takes_only_its_calls():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert kivi.kivi_status_string(s).startswith("KIVI_")
+    assert kivi.kivi_status_string(kivi.KIVI_ERR_DEVICE_ASSERT) == "KIVI_ERR_DEVICE_ASSERT"
+
+
+def test_status_word_in_layout():
+    """The 256-byte status sub-array follows the rings, 256-byte aligned, and ends the pool."""
+    c = cfg()
+    h = kivi.kivi_cache_create(c, 1 << 20, 1 << 40)
+    try:
+        lay = kivi.kivi_cache_layout(h)
+        assert lay["status"] % 256 == 0 and lay["status"] >= lay["v_ring"] + 32 * 8 * lay["ring_bytes"]
+        assert lay["total_bytes"] == lay["status"] + 256 == kivi.kivi_cache_pool_bytes(c)
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_check_device_errors(None)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+    finally:
+        kivi.kivi_cache_destroy(h)
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -73,3 +73,38 @@ def test_fused_step_largest_key_group():
                       num_seqs=3, seq_lens=[250, 255, 511], extra_tokens=8, shuffle=True, pool_factor=1.5,
                       n_outlier=2)
     _run(w, 8)
+
+
+# ---- the Llama decode layer's shape (G = 64, Gv = 128, R = 128, fp16, 16-token pages) across
+# Key flushes: a flush quantises R / G groups in the two Key waves of the appending work group
+# ("4.4 KV Cache 量化", section 3.2: the Key residual is quantised in one batch once it fills).
+
+def test_fused_step_llama_shape_two_group_flush():
+    """R / G = 2, as the Llama decode workload: sequences start 1..8 tokens before a
+    flush (T0 = 120..127 mod 128), so each step sequence crosses one flush of two
+    64-token groups within 10 steps; one sequence is long enough to be split."""
+    w = inputs.config(2, num_seqs=8, seq_lens=[120, 249, 378, 507, 636, 765, 894, 4095], extra_tokens=10,
+                      shuffle=True, pool_factor=1.25)
+    _run(w, 10)
+
+
+def test_fused_step_llama_shape_two_flushes_in_a_row():
+    """140 steps from T0 = 120..127 mod 128: every sequence crosses two flushes (each of
+    two Key groups), and every Value quad of the window turns over."""
+    w = inputs.config(2, num_seqs=4, seq_lens=[120, 253, 383, 1022], extra_tokens=140, shuffle=True,
+                      pool_factor=1.25)
+    _run(w, 140, check_every=5)
+
+
+def test_fused_step_four_group_flush():
+    """R / G = 4 (G = 64, R = 256)."""
+    w = inputs.config(2, num_seqs=6, seq_lens=[250, 251, 509, 766, 1020, 1279], extra_tokens=8, residual=256,
+                      shuffle=True, pool_factor=1.25)
+    _run(w, 8)
+
+
+def test_fused_step_sixteen_group_flush():
+    """R / G = 16 (G = 64, R = 1024): the two Key waves loop over 16 groups of one flush."""
+    w = inputs.config(2, num_seqs=4, seq_lens=[1020, 1023, 2046, 3071], extra_tokens=6, residual=1024,
+                      shuffle=True, pool_factor=1.25)
+    _run(w, 6)

@@ -4,7 +4,8 @@
   a seeded random order over a 1.25x pool): the whole cache state bit for bit, and
   every decode output against the oracle.
 * Ragged streaming batch (256 requests, lengths uniform in [128, 8192], int4, G = R = 64):
-  64 decode steps of one new token per request; after every step every byte the step
+  64 fused decode steps (kivi_decode_step: one new token per request appended and
+  attended in one launch, the call the benchmark times); after every step every byte the step
   changed (evicted Value token pages, flushed Key groups and their metadata, all
   residual windows) is compared bit for bit with the oracle, decode outputs of 16
   requests per step (all 256 over four passes) against the oracle; after the last step
@@ -94,7 +95,9 @@ def test_ragged_stream_64_steps_full_size():
         before = lens.copy()
         ks = [streams[s][0][lens[s]:lens[s] + 1] for s in range(S)]
         vs = [streams[s][1][lens[s]:lens[s] + 1] for s in range(S)]
-        gc.append(ks, vs)
+        q = w.q_decode(step)
+        # the call the benchmark times: append and attention in one launch
+        got = gc.decode_step(np.concatenate(ks), np.concatenate(vs), q, SCALE)
         for s in range(S):
             orcs[s].append(ks[s], vs[s])
         lens += 1
@@ -107,8 +110,6 @@ def test_ragged_stream_64_steps_full_size():
             pages.extend(gc.bt_np[s, tk0 // w.block_size: tk1 // w.block_size].tolist())
         mirror.refresh(pages)
         check_decode_step_state(mirror, gc.bt_np, orcs, before, lens, label=f"ragged stream step {step}")
-        q = w.q_decode(step)
-        got = gc.decode(q, SCALE)
         sample = [(16 * step + i) % S for i in range(16)]
         ref = oracle.attention_all([orcs[s] for s in sample], w.num_q_heads, q[sample], w.dtype,
                                    np.arange(len(sample) + 1), SCALE, False, threads=THREADS)

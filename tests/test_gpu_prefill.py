@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from kivi_quantized_kv_append_amd import inputs
-from harness import SCALE, GpuCache, check_attention, oracle_caches
+from harness import SCALE, GpuCache, check_attention, compare_seq_state, oracle_caches
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -57,27 +57,44 @@ def test_prefill_gqa_extremes(g):
     _prefill_case(w, [40, 25], causal=True)
 
 
-def test_prefill_qwen_full_size_sampled():
+def test_prefill_qwen_full_size():
     """Full Qwen2.5-7B prefill workload (8 requests x 16384 cached + a 512-token
     chunk, bf16, int4 G=R=128), in the launch configuration the benchmark times:
-    the chunk is bulk-appended in one call, every output is computed, and a
-    sample of (row, head) outputs is checked against the oracle, including the
-    first and last row of every request."""
+    the chunk is bulk-appended in one call (split over parts), after which the
+    whole cache state of every (request, KV head) is compared bit for bit with
+    the oracle; every output is computed, every (row, head) output of one
+    request (all 512 rows, all 28 heads) is checked against the oracle, and a
+    sample across the other requests, including the first and last row of
+    every request."""
     w = inputs.config(5)
     S, C, P = w.num_seqs, w.extra_tokens, int(w.seq_lens[0])
     gc = GpuCache(w)
-    rk, rv = zip(*[w.kv_stream(s) for s in range(S)])
+    rk, rv = zip(*w.kv_streams(16))
     gc.append([r[:P] for r in rk], [r[:P] for r in rv])
     gc.append([r[P:] for r in rk], [r[P:] for r in rv])
     orc = oracle_caches(w, lens=w.final_lens)
+    pv = gc.pool_view()
+    for s in range(S):
+        for h in range(w.num_kv_heads):
+            st = pv.seq_state(gc.bt_np[s], s, int(w.final_lens[s]), h)
+            compare_seq_state(st, orc[s], h, label=f"qwen full-size cache seq {s} head {h}")
+    del pv
+    print("[qwen full size] cache state bit-exact for every (request, KV head)", flush=True)
     cu = np.arange(0, (S + 1) * C, C)
     q = inputs.to_bits(np.random.default_rng(7).standard_normal((S * C, w.num_q_heads, 128)), w.dtype)
     got = gc.prefill(q, cu, SCALE, causal=True)
+    # one whole request: every row and head
+    s_full = 5
+    rows = np.repeat(np.arange(s_full * C, (s_full + 1) * C, dtype=np.int32), w.num_q_heads)
+    heads = np.tile(np.arange(w.num_q_heads, dtype=np.int32), C)
+    ref = oracle.attention(orc, w.num_q_heads, q, w.dtype, cu, SCALE, True, rows, heads, threads=16)
+    check_attention(got[rows, heads], ref, w.dtype, label=f"qwen full-size prefill, request {s_full}, every output")
+    print(f"[qwen full size] request {s_full}: all {C} x {w.num_q_heads} outputs within tolerance", flush=True)
     rng = np.random.default_rng(5)
     rows = np.concatenate([np.arange(0, S * C, C), np.arange(C - 1, S * C, C),
                            rng.integers(0, S * C, 200)]).astype(np.int32)
     heads = rng.integers(0, w.num_q_heads, rows.size).astype(np.int32)
-    ref = oracle.attention(orc, w.num_q_heads, q, w.dtype, cu, SCALE, True, rows, heads, threads=8)
+    ref = oracle.attention(orc, w.num_q_heads, q, w.dtype, cu, SCALE, True, rows, heads, threads=16)
     check_attention(got[rows, heads], ref, w.dtype, label="qwen full-size prefill (sampled)")
 
 
