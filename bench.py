@@ -82,6 +82,51 @@ def decode_bytes(lens, w) -> int:
     return total
 
 
+def capacity_report(kivi, inputs, budget: int = 1 << 30) -> dict:
+    """Capacity of each workload's cache layout ("S4 KV": about three times the fp16
+    KV tokens per GPU; "4.4 KV Cache 量化", section 1: M_KV), through the C ABI:
+    tokens a per-layer budget holds (residual rings for the workload's requests
+    included) against fp16 K/V, and, for one sequence of T tokens, the shares of
+    codes, group metadata and the residual ring in its bytes ("4.4 KV Cache 量化",
+    section 3.2: the shorter the context, the more the full-precision residual and
+    the metadata weigh)."""
+    out = {}
+    for cfg_id in (1, 2, 3, 4, 5):
+        w = inputs.config(cfg_id)
+        H, es = w.num_kv_heads, 2
+        cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, 1, w.num_seqs, w.dtype)
+        _, tokens = kivi.kivi_cache_capacity(cfg, budget)
+        fp16_tokens = budget // (2 * H * 128 * es)
+        per_seq = []
+        for T in (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+            b = sequence_bytes(kivi, w, T)
+            per_seq.append({"T": T, "bytes": b["total"], "codes_share": round(b["codes"] / b["total"], 4),
+                            "meta_share": round(b["meta"] / b["total"], 4),
+                            "residual_share": round(b["residual"] / b["total"], 4),
+                            "density_vs_fp16": round(2 * T * H * 128 * es / b["total"], 3)})
+        out[w.name] = {"bits": w.bits, "k_group": w.k_group, "v_group": w.v_group, "residual": w.residual,
+                       "kv_heads": H, "budget_bytes": budget, "kv_tokens": tokens, "fp16_kv_tokens": fp16_tokens,
+                       "density_vs_fp16": round(tokens / fp16_tokens, 3), "per_sequence": per_seq}
+    return out
+
+
+def sequence_bytes(kivi, w, T: int) -> dict:
+    """Bytes one sequence of T tokens holds in w's layout (one layer, all KV heads): its
+    pages' codes and group metadata (from the C ABI's layout) and its residual ring."""
+    H = w.num_kv_heads
+    pages = -(-T // w.block_size)
+    cfg = kivi.make_config(H, w.bits, w.k_group, w.v_group, w.residual, w.block_size, pages, 1, w.dtype)
+    h = kivi.kivi_cache_create(cfg, 1 << 20, kivi.kivi_cache_pool_bytes(cfg))
+    try:
+        lay = kivi.kivi_cache_layout(h)
+    finally:
+        kivi.kivi_cache_destroy(h)
+    codes = 2 * pages * H * lay["code_bytes"]
+    meta = pages * H * (lay["k_meta_bytes"] + lay["v_meta_bytes"])
+    residual = 2 * H * lay["ring_bytes"]
+    return {"codes": codes, "meta": meta, "residual": residual, "total": codes + meta + residual}
+
+
 def prefill_flop(cached: int, chunk: int, num_q_heads: int, num_seqs: int, d: int = 128) -> int:
     """Useful FLOP of causal chunked prefill: query i of a chunk sees cached + i + 1
     tokens; QK^T and PV each take 2 d FLOP per (query, head, visible token)."""
@@ -368,7 +413,7 @@ def flush_leg(torch, kivi, inputs, dev, check: bool, n_samples: int = 20, n_chec
     the 128-token Key residual of every (request, KV head), so kivi_decode_step
     quantises two 64-token Key groups per pair beside the attention. Each sample
     restores the cache from a pristine copy and evicts the last-level cache with a
-    512 MB write before each timed step (one HIP event pair per step)."""
+    512 MB read before each timed step (one HIP event pair per step)."""
     w = inputs.config(2, seq_lens=np.full(32, 4222), extra_tokens=2)
     S, H, HQ, d = w.num_seqs, w.num_kv_heads, w.num_q_heads, 128
     T0 = int(w.seq_lens[0])
@@ -400,7 +445,7 @@ def flush_leg(torch, kivi, inputs, dev, check: bool, n_samples: int = 20, n_chec
     ws_bytes = kivi.kivi_decode_workspace_bytes(h, S, HQ, msl)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((S, HQ, d), dtype=torch.int16, device=dev)
-    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evict = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MB, read (not written) to evict
     stream = torch.cuda.Stream()
     scale = 1.0 / math.sqrt(d)
     t = {0: [], 1: []}
@@ -409,7 +454,7 @@ def flush_leg(torch, kivi, inputs, dev, check: bool, n_samples: int = 20, n_chec
         for smp in range(n_samples + 1):
             pool.copy_(pristine)
             for i in range(2):
-                evict.fill_(smp & 0xFF)
+                evict.sum()  # reads 512 MB: the last-level cache holds clean lines of another buffer
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 kivi.kivi_decode_step(h, S, HQ, step_q[i], slots, lens_before[i], step_k[i], step_v[i], msl, bt,
@@ -427,7 +472,8 @@ def flush_leg(torch, kivi, inputs, dev, check: bool, n_samples: int = 20, n_chec
            "step_no_flush": _dist(np.array(t[0])) | {"bytes": decode_bytes(np.full(S, T0 + 1), w)},
            "step_key_flush": _dist(np.array(t[1])) | {"bytes": decode_bytes(np.full(S, T0 + 2), w)},
            "note": "kivi_decode_step on a cache restored from a pristine copy, the last-level cache evicted "
-                   "before each step; the flush step quantises 2 Key groups of 64 tokens per (request, KV head)"}
+                   "(a 512 MB read) before each step; the flush step quantises 2 Key groups of 64 tokens per "
+                   "(request, KV head)"}
     if check:
         import oracle
         caches = []
@@ -905,13 +951,11 @@ def main():
         "parity": parity,
         "input_gen_s": round(gen_s, 1),
     }
-    # capacity of a 1 GiB per-layer budget in this workload's layout, against fp16 K/V
-    budget = 1 << 30
-    _, cap_tokens = kivi.kivi_cache_capacity(cfg, budget)
-    fp16_tokens = budget // (2 * H * d * 2)
-    res["capacity"] = {"budget_bytes": budget, "kv_tokens": cap_tokens, "fp16_kv_tokens": fp16_tokens,
-                       "density_vs_fp16": round(cap_tokens / fp16_tokens, 3),
-                       "note": f"one layer, {H} KV heads, residual rings for {S} sequences included"}
+    # capacity of a 1 GiB per-layer budget in each workload's layout, against fp16 K/V, and the
+    # residual and metadata shares against context length
+    res["capacity"] = capacity_report(kivi, inputs) | {
+        "note": "one layer, all KV heads; kv_tokens: pages of a 1 GiB pool with residual rings for the "
+                "workload's requests; per_sequence: one sequence of T tokens (its pages and its ring)"}
     for h in handles:
         kivi.kivi_cache_destroy(h)
     del pools, step_k, step_v, step_q

@@ -333,8 +333,7 @@ namespace kivi {
 //     per Gv-channel group) and the new token's residual writes; one wave,
 //     channels 2 lane and 2 lane + 1.
 //   append_token_key_wave: when the Key residual fills, its R tokens' Key
-//     groups for channels [64 half, 64 half + 64), one channel per lane; two
-//     waves (half 0 and 1); scratch: kMaxG * 64 bytes of the wave's LDS.
+//     groups for channels [64 half, 64 half + 64); two waves (half 0 and 1).
 // The caller waits for the stores to complete and synchronises before any
 // wave reads what these write.
 // ---------------------------------------------------------------------------
@@ -456,82 +455,144 @@ __device__ __forceinline__ void append_token_value_wave(const AppendArgs& a, int
     t.ringV[vring_index(R, slot_new, 2 * lane + 1)] = (uint16_t)(vv >> 16);
 }
 
+// Key flush of one wave: channels [64 half, 64 half + 64) of every Key group
+// the token completes. Lane (u = lane / 8, c = lane % 8) holds channels
+// 8 (8 half + c) .. + 7 of tokens u, u + 8, ...: one 16-byte load per token
+// and lane, a chunk of up to 64 tokens (and its page ids) in flight together,
+// so the residual is read in one round trip per chunk rather than one per
+// token. A group longer than a chunk is read twice (min / max, then codes).
+// Eight consecutive channels of one token are exactly one int4 code word of
+// the Key layout (slot (token, j), word w with 32 w + 8 j = the chunk's first
+// channel); an int2 word joins the chunks c and c ^ 4 of lanes lane and
+// lane ^ 4.
 template <int BITS, int DT>
-__device__ __forceinline__ void append_token_key_wave(const AppendArgs& a, int s, int h, int half, int lane,
-                                                      uint8_t* scratch) {
+__device__ __forceinline__ void append_token_key_wave(const AppendArgs& a, int s, int h, int half, int lane) {
     constexpr int QMAX = (1 << BITS) - 1;
     constexpr int TILE_BYTES = kTile * kHeadDim * BITS / 8;
     constexpr int SLOT_BYTES = 4 * BITS;
+    constexpr int kChunk = 64;        // tokens loaded together
+    constexpr int kHeld = kChunk / 8;  // of them per lane
     const TokenAppend t = token_append_ctx(a, s, h);
     if (!t.ok) return;
     const CacheView& V = *t.V;
     const int T0 = t.T0, T1 = T0 + 1, R = t.R, G = t.G, Bk = t.Bk;
     const int TK0 = R * (T0 / R), TK1 = R * (T1 / R);
     if (TK1 == TK0) return;
-    const int c = 64 * half + lane;
+    const int u = lane >> 3, cl = lane & 7;
+    const int chunk = 8 * half + cl;  // channels 8 chunk .. 8 chunk + 7
+    const int c0 = 8 * chunk;
     const int nch = kHeadDim * Bk / G;
-    auto kval = [&](int p) -> float {
-        const uint16_t u = p < T0 ? t.ringK[(size_t)(p % R) * kHeadDim + c] : t.inK[c];
-        return canon(to_f32<DT>(u));
+    const int cw = G < kChunk ? G : kChunk;  // tokens per chunk (G is a power of two)
+    const int nheld = cw / 8;
+    uint4 held[kHeld];
+    int pg = -1;
+    // tokens c_start + u + 8 i of one chunk, and its page ids (lane l < cw / Bk:
+    // the page of position c_start + l Bk)
+    auto load_chunk = [&](int c_start) {
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i) {
+            if (i >= nheld) break;
+            const int p = c_start + u + 8 * i;
+            const uint16_t* src = p < T0 ? t.ringK + (size_t)(p % R) * kHeadDim + c0 : t.inK + c0;
+            held[i] = *reinterpret_cast<const uint4*>(src);
+        }
+        pg = lane * Bk < cw ? t.page_of(c_start + lane * Bk) : -1;
     };
-    for (int j = TK0 / G; j < TK1 / G; ++j) {
-        const int base = j * G;
-        float mn = INFINITY, mx = -INFINITY;
-        for (int i = 0; i < G; ++i) {
-            const float x = kval(base + i);
-            mn = fminf(mn, x);
-            mx = fmaxf(mx, x);
+    auto value = [&](const uint4& w, int e) -> float {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        return canon(to_f32<DT>((uint16_t)(ws[e >> 1] >> (16 * (e & 1)))));
+    };
+    for (int base = TK0; base < TK1; base += G) {
+        float mn[8], mx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            mn[e] = INFINITY;
+            mx[e] = -INFINITY;
         }
-        uint16_t s16, z16;
-        float S, Z;
-        group_params(mn, mx, QMAX, s16, z16, S, Z);
-        const int mblk = t.page_of(base + (c / nch) * Bk);
-        if (mblk >= 0) {
-            uint16_t* meta = reinterpret_cast<uint16_t*>(V.k_meta + ((size_t)mblk * t.H + h) * V.k_meta_bytes);
-            meta[c % nch] = s16;
-            meta[nch + c % nch] = z16;
-        }
-        for (int i = 0; i < G; ++i) scratch[i * 64 + lane] = (uint8_t)group_code(kval(base + i), S, Z, QMAX);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // code words of this wave's channels: int4 words (token, w, jj) with
-        // w in {2 half, 2 half + 1}; int2 words with w = half
-        constexpr int WPT = (BITS == 4) ? 8 : 4;  // words per token from 64 channels
-        for (int q = lane; q < G * WPT; q += 64) {
-            const int i = q / WPT, k = q % WPT;
-            const int p = base + i;
-            const int blk = t.page_of(p);
-            if (blk < 0) continue;
-            const int sub = (p % Bk) / kTile, m = p % kTile;
-            const uint8_t* cd = scratch + i * 64;
-            uint32_t word = 0;
-            int jj, w;
-            if constexpr (BITS == 4) {
-                w = 2 * half + (k >> 2);
-                jj = k & 3;
-                const int cl = 32 * (w & 1) + 8 * jj;  // local channel of 32 w + 8 jj
-                for (int e = 0; e < 4; ++e) {
-                    word |= (uint32_t)cd[cl + 2 * e] << (4 * e);
-                    word |= (uint32_t)cd[cl + 2 * e + 1] << (16 + 4 * e);
-                }
-            } else {
-                w = half;
-                jj = k;
-                const int cl0 = 8 * jj, cl1 = cl0 + 32;  // local channels of 64 w + 8 jj, + 32
-                for (int f = 0; f < 8; ++f) {
-                    const int b = (f < 4 ? cl0 : cl1) + 2 * (f & 3);
-                    word |= (uint32_t)cd[b] << (2 * f);
-                    word |= (uint32_t)cd[b + 1] << (16 + 2 * f);
+        for (int c_start = base; c_start < base + G; c_start += cw) {
+            load_chunk(c_start);
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) {
+                if (i >= nheld) break;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = value(held[i], e);
+                    mn[e] = fminf(mn[e], x);
+                    mx[e] = fmaxf(mx[e], x);
                 }
             }
-            uint8_t* dst = V.k_codes + ((size_t)blk * t.H + h) * V.code_bytes + sub * TILE_BYTES +
-                           SLOT_BYTES * (m + 16 * jj) + 4 * w;
-            *reinterpret_cast<uint32_t*>(dst) = word;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // over the chunk's 8 lanes (cl + 8 u), then the group's parameters
+        float S[8], Z[8];
+        uint32_t sp[4], zp[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+            for (int o = 8; o < 64; o <<= 1) {
+                mn[e] = fminf(mn[e], __shfl_xor(mn[e], o, 64));
+                mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o, 64));
+            }
+            uint16_t s16, z16;
+            group_params(mn[e], mx[e], QMAX, s16, z16, S[e], Z[e]);
+            if (e & 1) {
+                sp[e >> 1] |= (uint32_t)s16 << 16;
+                zp[e >> 1] |= (uint32_t)z16 << 16;
+            } else {
+                sp[e >> 1] = s16;
+                zp[e >> 1] = z16;
+            }
+        }
+        // the chunk's 8 scales and 8 zero-points, contiguous in the Key meta of
+        // the group's page that holds them (nch is a multiple of 8)
+        if (u == 0) {
+            const int mblk = t.page_of(base + (c0 / nch) * Bk);
+            if (mblk >= 0) {
+                uint16_t* meta = reinterpret_cast<uint16_t*>(V.k_meta + ((size_t)mblk * t.H + h) * V.k_meta_bytes);
+                *reinterpret_cast<uint4*>(meta + c0 % nch) = (uint4){sp[0], sp[1], sp[2], sp[3]};
+                *reinterpret_cast<uint4*>(meta + nch + c0 % nch) = (uint4){zp[0], zp[1], zp[2], zp[3]};
+            }
+        }
+        for (int c_start = base; c_start < base + G; c_start += cw) {
+            if (cw < G) load_chunk(c_start);  // else the chunk is still held
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) {
+                if (i >= nheld) break;
+                const int p = c_start + u + 8 * i;
+                uint32_t q[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = group_code(value(held[i], e), S[e], Z[e], QMAX);
+                const int blk = __shfl(pg, (p - c_start) / Bk, 64);
+                const int sub = (p % Bk) / kTile, m = p % kTile;
+                uint32_t word;
+                int w, jj;
+                bool store = blk >= 0;
+                if constexpr (BITS == 4) {
+                    // even channels in bits 4e, odd channels in bits 16 + 4e
+                    word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) word |= (q[2 * e] << (4 * e)) | (q[2 * e + 1] << (16 + 4 * e));
+                    w = chunk >> 2;
+                    jj = chunk & 3;
+                } else {
+                    // this chunk's fields: channel 8 chunk + 2 e + {0, 1} in fields e + 4 hi
+                    // and 8 + e + 4 hi (hi: the chunk is the word's second channel group)
+                    const int hi = (chunk >> 2) & 1;
+                    uint32_t part = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        part |= (q[2 * e] << (2 * (e + 4 * hi))) | (q[2 * e + 1] << (2 * (8 + e + 4 * hi)));
+                    word = part | (uint32_t)__shfl_xor((int)part, 4, 64);
+                    w = chunk >> 3;
+                    jj = chunk & 3;
+                    store = store && hi == 0;
+                }
+                if (store) {
+                    uint8_t* dst = V.k_codes + ((size_t)blk * t.H + h) * V.code_bytes + sub * TILE_BYTES +
+                                   SLOT_BYTES * (m + 16 * jj) + 4 * w;
+                    *reinterpret_cast<uint32_t*>(dst) = word;
+                }
+            }
+        }
     }
 }
 

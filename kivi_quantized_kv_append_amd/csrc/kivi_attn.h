@@ -353,11 +353,20 @@ __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return _
 // both, with k = (tile A tokens 4j..4j+3, tile B tokens 4j..4j+3) in each
 // lane; its A-operand holds the codes, its B-operand the fp16 weights
 // p * scale / F (F: the place value of the token's code field). Zero-points
-// go through zacc. With `only_a` tile B's weights are zero.
+// go through zacc. A tile that is not computed (oka / okb false: outside the
+// wave's range, or without a page) has zero weights, and its metadata, loaded
+// from whatever page 0 holds, is replaced by zeros: 0 times a NaN or infinite
+// scale left in an unused page would otherwise poison the accumulators.
 template <int BITS, int NG, int NB>
-__device__ __forceinline__ void value_pair(Acc<NG, NB>& st, const uint32_t* vwa, const uint32_t* vma,
-                                           const uint32_t* vwb, const uint32_t* vmb, const float pa[4],
-                                           const float pb[4]) {
+__device__ __forceinline__ void value_pair(Acc<NG, NB>& st, const uint32_t* vwa, const uint32_t* vma_in,
+                                           const uint32_t* vwb, const uint32_t* vmb_in, const float pa[4],
+                                           const float pb[4], bool oka, bool okb) {
+    uint32_t vma[4 * NG], vmb[4 * NG];
+#pragma unroll
+    for (int k = 0; k < 4 * NG; ++k) {
+        vma[k] = oka ? vma_in[k] : 0u;
+        vmb[k] = okb ? vmb_in[k] : 0u;
+    }
     constexpr float kF23 = (BITS == 4) ? 0.0625f : 0.25f;  // 1/F of tokens r = 2, 3
     const h2 qa01 = {(_Float16)pa[0], (_Float16)pa[1]};
     const h2 qa23 = {(_Float16)(pa[2] * kF23), (_Float16)(pa[3] * kF23)};

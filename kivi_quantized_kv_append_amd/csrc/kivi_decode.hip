@@ -48,6 +48,12 @@ constexpr int kWaves = 8;
 // younger wave takes 200 minus this): measured best at 130 on MI355X.
 constexpr int kOldShare = 130;
 constexpr int kAppendShare = 70;  // main-tile share of the appending wave (20-70 measure alike)
+// Main-tile weight of each of the two Key-flush waves on a step that flushes
+// (an even share is 300; their share goes to waves 0-3): the flush keeps them
+// busy for a third of the step (measured 52.8 us per Llama flush step against
+// 61.0 us at the plain share, 43.5 us with no flush arithmetic at all).
+constexpr int kFlushShare = 40;
+static_assert((4 * (200 - kOldShare) - kAppendShare - kFlushShare) % 2 == 0, "waves 0-3 split the rest evenly");
 // Main tiles keep the 1024 offsets of the Key codes (one and-or per pair, no
 // subtract) and take 1024 sum_c Q'[n][c] out of the table's bias; the tail
 // tiles, whose tables are built apart, use exact codes.
@@ -236,7 +242,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // they take the larger share and the pair ends together.
     // In a fused step the last wave also appends, so it takes kAppendShare
     // and waves 4-6 share the rest of the younger half.
+    const bool flush_step = a.fuse && T > 0 && T % R == 0;  // this step fills the Key residual (uniform)
     auto weight = [&](int wv) -> int {
+        if (flush_step && wv >= kWaves - 3 && wv < kWaves - 1) return kFlushShare;
+        if (flush_step && wv < 4) return 3 * kOldShare + (4 * (200 - kOldShare) - kAppendShare - kFlushShare) / 2;
         if (wv < 4) return 3 * kOldShare;
         if (!a.fuse) return 3 * (200 - kOldShare);
         return wv == kWaves - 1 ? 3 * kAppendShare : 4 * (200 - kOldShare) - kAppendShare;
@@ -257,7 +266,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // Value token leaving the window (t_evict) depends on the append; the
     // appending wave takes it, the other waves the rest in the prologue. A
     // flush step takes every tail tile after a barrier at the end.
-    const bool flush_step = a.fuse && T > 0 && T % R == 0;  // uniform
     const int t_evict = (a.fuse && T - 1 >= R) ? (T - 1 - R) / kTile : -1;
     const bool skip_evict = a.fuse && !flush_step && t_evict >= 0;
     const int n_tail_dealt = n_tail - (skip_evict ? 1 : 0);
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 pb[r] = okb ? st.weight(rb[r], sl2) : 0.0f;
             }
             st.l_acc += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
-            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb);
+            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb, oka, okb);
         }
     };
 
@@ -563,8 +571,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 tail_compute(t_evict, x);
             }
         } else if (wave >= kWaves - 3) {
-            uint8_t* scratch = smem + kWaves * wave_lds_bytes(g) + (wave - (kWaves - 3)) * kMaxG * 64;
-            append_token_key_wave<BITS, DT>(a.app, c.s, c.h, wave - (kWaves - 3), lane, scratch);
+            // the flush is on the step's critical path: the flush waves, younger
+            // than the streaming wave on their SIMD, take issue priority for it
+            __builtin_amdgcn_s_setprio(3);
+            append_token_key_wave<BITS, DT>(a.app, c.s, c.h, wave - (kWaves - 3), lane);
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     if (m_begin < m_end) {
@@ -750,10 +761,8 @@ int launch_decode_step(const CacheView& v, int num_seqs, int num_q_heads, const 
     a.app.block_table = block_table;
     a.app.bt_stride = bt_stride;
     a.app.mode = 0;
-    const size_t lds = std::max(plan.lds_bytes, (size_t)kWaves * wave_lds_bytes(num_q_heads / v.H) +
-                                                    2 * (size_t)kMaxG * 64);  // + Key-flush scratch
     return launch_decode_args(a, v, num_seqs, num_q_heads, q, slot_ids, seq_lens_before, block_table, bt_stride,
-                              softmax_scale, out, partials, plan, lds, stream);
+                              softmax_scale, out, partials, plan, plan.lds_bytes, stream);
 }
 
 namespace {

@@ -154,6 +154,18 @@ __device__ __forceinline__ uint32_t f8_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 0.00390625f, kHigh));
 }
 
+// Value bytes of tokens at or past T (a sequence's last, partial tile) are
+// never written and may hold an E4M3 NaN; their weights are 0, and 0 times NaN
+// is NaN, so they are cleared: byte r of each word is token p0 + r.
+__device__ __forceinline__ void mask_past_end(uint32_t vw[8], int p0, int T) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (p0 + r < T) keep |= 0xFFu << (8 * r);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) vw[tt] &= keep;
+}
+
 struct F8Tile {
     uint4 k[2], v[2];
     bool ok;
@@ -290,7 +302,8 @@ __global__ __launch_bounds__(kF8DecThreads, 1) void fp8_decode_kernel(F8DecodeAr
             B[r] = hi;
             B[4 + r] = lo;
         }
-        const uint32_t vw[8] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w, x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
+        uint32_t vw[8] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w, x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
+        if (kTile * t + kTile > T) mask_past_end(vw, p0, T);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
             const h4 A = make_h4(f8_pair<false>(vw[tt]), f8_pair<true>(vw[tt]));
@@ -552,7 +565,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArg
             B[r] = hi;
             B[4 + r] = lo;
         }
-        const uint32_t vw[8] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w, x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
+        uint32_t vw[8] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w, x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
+        if (kTile * t + kTile > T) mask_past_end(vw, p0, T);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
             const h4 A = make_h4(f8_pair<false>(vw[tt]), f8_pair<true>(vw[tt]));

@@ -69,6 +69,7 @@ size_t decode_lds_bytes(int gqa);
 
 constexpr int kPartialStride = 132;  // floats per partial: m, l, pad, pad, o[128]
 
+
 // Work groups per (sequence, KV head) for the quantisation phase of an
 // append of up to max_new rows per sequence: one part per 64 new rows, at
 // most 64 parts. One part runs the whole append in a single launch.

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
                 }
             }
             st.l_acc += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
-            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb);
+            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb, oka, okb);
         }
     };
     if (m_end > 0) {

@@ -267,7 +267,8 @@ def check_decode_step_state(mirror: PoolMirror, bt_np: np.ndarray, orcs: list, l
 # ---------------------------------------------------------------------------
 
 class GpuCache:
-    def __init__(self, w: inputs.Workload, device="cuda", fill_garbage: bool = True, num_blocks=None):
+    def __init__(self, w: inputs.Workload, device="cuda", fill_garbage: bool = True, num_blocks=None,
+                 fill_byte=None):
         import torch
         self.torch = torch
         self.w = w
@@ -278,7 +279,9 @@ class GpuCache:
         self.cfg = kivi.make_config(w.num_kv_heads, w.bits, w.k_group, w.v_group, w.residual,
                                     w.block_size, nb, w.num_seqs, w.dtype, v_flush=w.v_flush)
         self.nbytes = kivi.kivi_cache_pool_bytes(self.cfg)
-        if fill_garbage:
+        if fill_byte is not None:  # e.g. 0xFF: every unwritten fp16 / bf16 value is a NaN
+            self.pool = torch.full((self.nbytes,), fill_byte, dtype=torch.uint8, device=device)
+        elif fill_garbage:
             g = torch.Generator(device="cpu").manual_seed(123)
             self.pool = torch.randint(0, 256, (self.nbytes,), dtype=torch.uint8, generator=g).to(device)
         else:
@@ -474,14 +477,17 @@ def fp8_decode_codes(chunks: np.ndarray, kind: str) -> np.ndarray:
 class Fp8GpuCache:
     """An FP8 cache of a workload's shape (its heads, pages and lengths) on the GPU."""
 
-    def __init__(self, w: inputs.Workload, k_scales, v_scales, per_head: bool, device="cuda"):
+    def __init__(self, w: inputs.Workload, k_scales, v_scales, per_head: bool, device="cuda", fill_byte=None):
         import torch
         self.torch, self.w, self.device = torch, w, device
         self.cfg = kivi.make_fp8_config(w.num_kv_heads, w.block_size, w.num_blocks, 1, w.dtype,
                                         scale_per_head=int(per_head))
         self.nbytes = kivi.kivi_cache_pool_bytes(self.cfg)
-        g = torch.Generator(device="cpu").manual_seed(321)
-        self.pool = torch.randint(0, 256, (self.nbytes,), dtype=torch.uint8, generator=g).to(device)
+        if fill_byte is not None:  # e.g. 0xFF: every unwritten E4M3 byte is a NaN
+            self.pool = torch.full((self.nbytes,), fill_byte, dtype=torch.uint8, device=device)
+        else:
+            g = torch.Generator(device="cpu").manual_seed(321)
+            self.pool = torch.randint(0, 256, (self.nbytes,), dtype=torch.uint8, generator=g).to(device)
         self.handle = kivi.kivi_cache_create(self.cfg, self.pool, self.nbytes)
         self.layout = kivi.kivi_cache_layout(self.handle)
         self.bt_np = w.block_table()

@@ -316,3 +316,34 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_capacity_report_pins_to_m_kv():
+    """The capacity report of every workload layout: a sequence's code bytes are the
+    M_KV formula at b bits for its pages ("4.4 KV Cache 量化", section 1), its group
+    metadata is 4 bytes per (Key group, channel) and per (token, Value group), its
+    residual ring is 2 R H 128 bytes per tensor; the residual and metadata share falls
+    as the context grows ("4.4 KV Cache 量化", section 3.2) and density approaches
+    16 / (b + metadata bits) against fp16."""
+    import bench
+    from kivi_quantized_kv_append_amd import inputs
+    for cfg_id in (1, 2, 3, 4, 5):
+        w = inputs.config(cfg_id)
+        H, Bk = w.num_kv_heads, w.block_size
+        prev = None
+        for T in (128, 512, 4096, 32768):
+            b = bench.sequence_bytes(kivi, w, T)
+            pages = -(-T // Bk)
+            assert b["codes"] == oracle.m_kv_bytes(1, 1, pages * Bk, H, 128, w.bits)
+            groups = -(-pages * Bk // w.k_group)
+            assert b["meta"] == H * (groups * 128 * 4 + pages * Bk * (128 // w.v_group) * 4)
+            assert b["residual"] == 2 * H * w.residual * 128 * 2
+            share = (b["meta"] + b["residual"]) / b["total"]
+            if prev is not None:
+                assert share < prev
+            prev = share
+    rep = bench.capacity_report(kivi, inputs)
+    assert set(rep) == {inputs.config(i).name for i in (1, 2, 3, 4, 5)}
+    llama = rep[inputs.config(2).name]
+    assert 3.0 < llama["density_vs_fp16"] < 4.0
+    assert llama["per_sequence"][-1]["density_vs_fp16"] > llama["per_sequence"][0]["density_vs_fp16"]

@@ -108,3 +108,17 @@ def test_fused_step_sixteen_group_flush():
     w = inputs.config(2, num_seqs=4, seq_lens=[1020, 1023, 2046, 3071], extra_tokens=6, residual=1024,
                       shuffle=True, pool_factor=1.25)
     _run(w, 6)
+
+
+def test_fused_step_residual_not_a_multiple_of_the_load_span():
+    """R = 192, G = 64: the flush waves load 128 residual tokens, then the last 64."""
+    w = inputs.config(2, num_seqs=3, seq_lens=[189, 383, 767], extra_tokens=5, residual=192, shuffle=True,
+                      pool_factor=1.25)
+    _run(w, 5)
+
+
+def test_fused_step_two_groups_of_256():
+    """R = 512, G = 256: each group is read in two spans of 128 tokens (min / max, then codes)."""
+    w = inputs.config(2, num_seqs=2, seq_lens=[509, 1535], extra_tokens=4, residual=512, k_group=256,
+                      shuffle=True, pool_factor=1.25)
+    _run(w, 4)
