@@ -287,6 +287,23 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
                                   float softmax_scale, void* d_out, void* d_ws, size_t ws_bytes,
                                   void* stream);
 
+/* kivi_decode_attention for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as kivi_decode_attention without the
+ * workspace: the split partials live in a static device array of 4 MiB per
+ * GPU, held from the first call on a device until the process ends. The
+ * call allocates nothing; on its first call on a device it looks up that
+ * device's copy of the array. Every call on one device shares the array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller. Nothing in the array needs to start at zero.
+ * A call whose partials need more than 4 MiB (num_seqs * H_Q * splits * 528
+ * bytes, see kivi_decode_workspace_bytes) returns KIVI_ERR_WORKSPACE.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.                       */
+kivi_status kivi_decode_attention_noalloc(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                          const void* d_q, const int32_t* d_slot_ids, const int32_t* d_seq_lens,
+                                          int32_t max_seq_len, const int32_t* d_block_table, int32_t bt_stride,
+                                          float softmax_scale, void* d_out, void* stream);
+
 /* One decode step in one launch: append one token per sequence (as
  * kivi_append_tokens with one row each: the Value eviction, the Key flush
  * when the residual fills, the residual write; "4.4 KV Cache 量化", section

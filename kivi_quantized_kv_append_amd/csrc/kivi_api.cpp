@@ -481,6 +481,41 @@ kivi_status kivi_decode_attention(const kivi_cache* cache, int32_t num_seqs, int
     return device_status(err, "decode launch");
 }
 
+kivi_status kivi_decode_attention_noalloc(const kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                          const void* d_q, const int32_t* d_slot_ids, const int32_t* d_seq_lens,
+                                          int32_t max_seq_len, const int32_t* d_block_table, int32_t bt_stride,
+                                          float softmax_scale, void* d_out, void* stream) {
+    kivi_status s = check_kivi_cache(cache);
+    if (s != KIVI_OK) return s;
+    s = check_heads(cache, num_q_heads);
+    if (s != KIVI_OK) return s;
+    if (num_seqs < 0) return fail(KIVI_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (max_seq_len < 0) return fail(KIVI_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (!d_q || !d_slot_ids || !d_seq_lens || !d_block_table || !d_out)
+        return fail(KIVI_ERR_INVALID_ARG, "a device pointer is NULL");
+    if (!aligned(d_q, 16) || !aligned(d_out, 16))
+        return fail(KIVI_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!aligned(d_slot_ids, 4) || !aligned(d_seq_lens, 4) || !aligned(d_block_table, 4))
+        return fail(KIVI_ERR_INVALID_ARG, "an int32 array is not 4-byte aligned");
+    if (bt_stride < 1) return fail(KIVI_ERR_INVALID_ARG, "bt_stride %d < 1", bt_stride);
+    if (!(softmax_scale == softmax_scale) || softmax_scale == std::numeric_limits<float>::infinity() ||
+        softmax_scale == -std::numeric_limits<float>::infinity())
+        return fail(KIVI_ERR_INVALID_ARG, "softmax_scale is not finite");
+    kivi::DecodePlan plan = kivi::decode_plan(cache, num_seqs, num_q_heads, max_seq_len);
+    if (plan.ws_bytes > kivi::kNoAllocScratchBytes)
+        return fail(KIVI_ERR_WORKSPACE, "the split partials need %zu bytes, more than the %zu-byte static scratch",
+                    plan.ws_bytes, kivi::kNoAllocScratchBytes);
+    float* partials = nullptr;
+    if (plan.ws_bytes > 0) {
+        if (int e = kivi::noalloc_scratch(&partials)) return device_status(e, "static scratch address");
+    }
+    if (int e = prepare_status(cache, stream)) return device_status(e, "status word clear");
+    int err = kivi::launch_decode(kivi::view_of(cache), num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_lens,
+                                  d_block_table, bt_stride, softmax_scale, d_out, partials, plan, stream);
+    return device_status(err, "decode launch");
+}
+
 kivi_status kivi_decode_step(kivi_cache* cache, int32_t num_seqs, int32_t num_q_heads, const void* d_q,
                              const int32_t* d_slot_ids, const int32_t* d_seq_lens_before, const void* d_k_new,
                              const void* d_v_new, int32_t max_seq_len, const int32_t* d_block_table,

@@ -34,6 +34,8 @@
 // of the evicted token is read by the wave that wrote it, and a flush step
 // reads its tail tiles after a barrier.
 
+#include <mutex>
+
 #include "kivi_append_body.h"
 #include "kivi_attn.h"
 
@@ -806,6 +808,29 @@ int launch_decode_args(DecodeArgs& a, const CacheView& v, int num_seqs, int num_
     return (int)hipGetLastError();
 }
 }  // namespace
+
+// Split partials of kivi_decode_attention_noalloc: one array per device,
+// held until the process ends, shared by every call on that device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+int noalloc_scratch(float** out) {
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        // the device's own copy of the array (the current device is `dev`)
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        ptrs[dev] = static_cast<float*>(p);
+    }
+    *out = ptrs[dev];
+    return 0;
+}
 
 size_t decode_lds_bytes(int g) {
     return std::max((size_t)kWaves * wave_lds_bytes(g), (size_t)merge_lds_bytes(g));

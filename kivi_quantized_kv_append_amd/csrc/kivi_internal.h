@@ -69,6 +69,12 @@ size_t decode_lds_bytes(int gqa);
 
 constexpr int kPartialStride = 132;  // floats per partial: m, l, pad, pad, o[128]
 
+// Static split-partial array of kivi_decode_attention_noalloc (per device).
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+constexpr int kMaxDevices = 64;
+// The calling thread's current device's copy of that array (its address is
+// looked up once per device); returns a hipError_t as int.
+int noalloc_scratch(float** out);
 
 // Work groups per (sequence, KV head) for the quantisation phase of an
 // append of up to max_new rows per sequence: one part per 64 new rows, at

@@ -35,7 +35,8 @@ KIVI_BF16 = 1
 
 EXPORTED = [
     "kivi_cache_pool_bytes", "kivi_cache_capacity", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_layout",
-    "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_step",
+    "kivi_append_tokens", "kivi_decode_workspace_bytes", "kivi_decode_attention", "kivi_decode_attention_noalloc",
+    "kivi_decode_step",
     "kivi_prefill_workspace_bytes", "kivi_prefill_attention", "kivi_prefill_attention_raw_chunk",
     "kivi_fp8_append_tokens", "kivi_fp8_decode_attention", "kivi_fp8_decode_step", "kivi_fp8_prefill_attention",
     "kivi_check_device_errors", "kivi_last_error",
@@ -87,6 +88,7 @@ def load():
         L.kivi_append_tokens.argtypes = [P, I32, P, P, P, I32, P, P, P, I32, P]
         L.kivi_decode_workspace_bytes.argtypes = [P, I32, I32, I32, c.POINTER(S)]
         L.kivi_decode_attention.argtypes = [P, I32, I32, P, P, P, I32, P, I32, c.c_float, P, P, S, P]
+        L.kivi_decode_attention_noalloc.argtypes = [P, I32, I32, P, P, P, I32, P, I32, c.c_float, P, P]
         L.kivi_decode_step.argtypes = [P, I32, I32, P, P, P, P, P, I32, P, I32, c.c_float, P, P, S, P]
         L.kivi_prefill_workspace_bytes.argtypes = [P, I32, I32, I32, I32, c.POINTER(S)]
         L.kivi_prefill_attention.argtypes = [P, I32, I32, P, P, I32, P, P, I32, P, I32, c.c_float,
@@ -199,6 +201,13 @@ def kivi_decode_attention(cache, num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_l
                                         _ptr(d_seq_lens), max_seq_len, _ptr(d_block_table), bt_stride,
                                         float(softmax_scale), _ptr(d_out), _ptr(d_ws), ws_bytes,
                                         _stream(stream)))
+
+
+def kivi_decode_attention_noalloc(cache, num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_lens, max_seq_len,
+                                  d_block_table, bt_stride, softmax_scale, d_out, stream=None):
+    _check(load().kivi_decode_attention_noalloc(cache, num_seqs, num_q_heads, _ptr(d_q), _ptr(d_slot_ids),
+                                                _ptr(d_seq_lens), max_seq_len, _ptr(d_block_table), bt_stride,
+                                                float(softmax_scale), _ptr(d_out), _stream(stream)))
 
 
 def kivi_decode_step(cache, num_seqs, num_q_heads, d_q, d_slot_ids, d_seq_lens_before, d_k_new, d_v_new,

@@ -102,6 +102,7 @@ static void abi() {
                        KIVI_ERR_WORKSPACE);
             EXPECT(kivi_decode_step(h, S, 32, D, I, I, D, D, T, I, 256, 0.088f, D, ws ? D : nullptr, ws, nullptr) ==
                    KIVI_OK);
+            EXPECT(kivi_decode_attention_noalloc(h, S, 32, D, I, I, T, I, 256, 0.088f, D, nullptr) == KIVI_OK);
         }
     EXPECT(kivi_decode_attention(h, 4, 30, D, I, I, 64, I, 1, 0.1f, D, D, 1 << 20, nullptr) == KIVI_ERR_UNSUPPORTED);
     EXPECT(kivi_decode_attention(h, 4, 32, D, I, I, 64, I, 1, NAN, D, D, 1 << 20, nullptr) == KIVI_ERR_INVALID_ARG);
