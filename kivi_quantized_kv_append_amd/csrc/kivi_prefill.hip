@@ -4,15 +4,26 @@
 // residual; "给 KV cache 减肥", section 3: values restored on read).
 //
 // Rows: the (query position, query head) pairs of one (sequence, KV head),
-// row r = i * g + head for chunk query i. A wave owns 16 consecutive rows
-// (one matrix-core row tile, the N dimension of the score MFMA) and streams
-// every Key/Value tile its rows can see: 16-token tiles of codes on matrix
-// cores exactly as in decode (Key scale folded into a per-group query table
-// split fp16 hi + lo, zero-point as the bias that starts the chain; Values in
-// pairs of tiles against fp16 weights p * scale / F), then the tiles that
-// touch the residual. Causal rows see tokens 0 .. their own position; the
-// mask is applied per row only on tiles past the smallest row position.
-// Work groups hold 4 independent waves; each wave writes its rows' output.
+// row r = i * g + head for chunk query i. A work group of 8 waves owns 256
+// consecutive rows, 32 per wave, and walks the 64-token tiles its rows can
+// see. Each tile is restored once per work group: each of its 512 threads
+// takes half of a 16-byte lane slot of Key codes and half of one of Value
+// codes and writes the restored values to LDS, Keys as [token][channel],
+// Values as [channel][token]. A restored Key k = code * scale + zero is kept
+// as an fp16 pair hi + lo (hi = fp16(k), lo = fp16(k - hi), about 22 bits):
+// outlier channels reach |k| of tens, where one fp16 rounding alone moves a
+// score by more than the attention tolerance allows. Values are restored to
+// fp16 with one packed FMA per pair (their rounding is averaged out).
+// Two LDS stages: the next tile's codes and metadata are loaded before the
+// current tile is computed and restored after it, one barrier per tile.
+// Per wave and tile, on matrix cores (v_mfma_f32_32x32x16_f16, fp32 sums):
+//   S^T[64 tokens][32 rows] = (K_hi + K_lo)[64][128] Q^T[128][32]   32 MFMAs
+//   online softmax per row (one lane pair per row), weights as fp16
+//   O^T[128][32] += V^T[128][64] P^T[64][32]                        16 MFMAs
+// The k-order of the P^T V MFMAs is the order in which the score MFMAs leave
+// the weights in the lanes; the Value rows in LDS are stored in that order.
+// Tiles that reach the residual, the end of the sequence or (second reading
+// below) the chunk are restored from the right source per token.
 //
 // Second reading of the prefill (the pages leave it open): with a chunk given
 // at full precision, the call comes before the chunk is stored; seq_lens are
@@ -29,13 +40,30 @@ namespace {
 
 using namespace attn;
 
-constexpr int kPWaves = 4;
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kRowsPerWave = 16;
-constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
-// Main-loop Key codes keep their 1024 offsets, taken out through the table's
-// bias (saves a packed subtract per code pair); the tail stays exact.
-constexpr bool kFoldK = true;
+constexpr int kRowsWave = 32;                 // query rows per wave (the N of the 32x32 MFMAs)
+constexpr int kRowsWg = kRowsWave * kPWaves;  // 256
+constexpr int kTileTok = 64;                  // tokens per KV tile: 4 sub-tiles of 16
+constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X, each with its own L2
+// LDS rows of one stage (fp16), padded by 16 bytes so that the 8 lanes a
+// 16-byte read serves per cycle fall on distinct banks:
+//   Key hi, Key lo  [64 tokens][128 channels + 8] each
+//   Value [128 channels][64 tokens + 8], the tokens of each 16-token k-step
+//         in the order the weights sit in the lanes (v_pos)
+constexpr int kKRow = kHeadDim + 8;
+constexpr int kVRow = kTileTok + 8;
+constexpr int kKHalfs = kTileTok * kKRow;     // one Key part
+constexpr int kVOff = 2 * kKHalfs;            // the Value rows within a stage
+constexpr int kStageHalfs = 2 * kKHalfs + kHeadDim * kVRow;
+// Key scales and zero-points of a tile, per 16-token sub-tile: [4][2][128] fp16
+// (the group of each sub-tile), in two stages of their own
+constexpr int kMetaHalfs = 4 * 2 * kHeadDim;
+constexpr size_t kPrefillLds = (2 * kStageHalfs + 2 * kMetaHalfs) * sizeof(_Float16);
+// Running-max threshold (log2 units): weights stay below 2^kLazy, rescales are rare
+constexpr float kLazy = 2.0f;
 
 struct PrefillArgs {
     CacheView v;
@@ -49,29 +77,42 @@ struct PrefillArgs {
     int bt_stride;
     int num_q_heads;
     int gqa;
-    float scale_log2;
+    float scale_log2;  // softmax scale * log2(e)
     int causal;
-    int max_q_len;   // the caller's bound of every query span
-    int wg_per_sh;   // work groups per (sequence, KV head)
-    int tpg_shift;   // log2(tiles per Key group)
-    int tpp_shift;   // log2(tiles per page)
-    uint32_t code_array_bytes, vmeta_array_bytes, kmeta_array_bytes;
+    int max_q_len;     // the caller's bound of every query span
+    int wg_per_sh;     // work groups per (sequence, KV head)
     uint16_t* out;
 };
 
-// LDS of one wave: q rows [16] | Key-group table rows [16][hi, lo] | bias [16]
-__host__ __device__ constexpr int prefill_wave_lds_bytes() { return 3 * kRowsPerWave * kRowBytes + 64; }
+// Position of token 4a + r of a 16-token k-step in a Value row: the lanes of
+// half h of a P^T V MFMA hold tokens 4h .. 4h + 3 and 8 + 4h .. 8 + 4h + 3 of
+// the k-step (in that order) as their 8 k-values, so blocks of 4 tokens are
+// stored in the order a = 0, 2, 1, 3.
+__device__ __forceinline__ int v_pos(int a) { return 8 * (a & 1) + 4 * (a >> 1); }
 
-// Tiles per load buffer (two buffers per wave), as in decode.
-template <int NG>
-constexpr int max_buffer_tiles_pf() { return NG == 1 ? 4 : (NG <= 4 ? 2 : 1); }
+// Exact fp16 pair of the two code fields at bit `sh` of each half of x.
+template <int BITS>
+__device__ __forceinline__ h2 code_pair(uint32_t x, int sh) {
+    const uint32_t m = magic_pair(x >> sh, BITS == 4 ? 0x000F000Fu : 0x00030003u);
+    return __builtin_bit_cast(h2, m) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+}
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-template <int BITS, int DT, int NG, int kHalf>
+// The codes a thread restores for one tile: half of its Key slot and of its
+// Value slot of sub-tile u, and the Value metadata of the slot's 4 tokens for
+// the groups of its channels.
+template <int BITS, int NGP>
+struct SlotRegs {
+    uint32_t k[BITS / 2], v[BITS / 2];
+    uint32_t vm[4 * NGP];
+};
+
+template <int BITS, int DT, int NG>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int TILE_BYTES = kTile * kHeadDim * BITS / 8;
     constexpr int SLOT_BYTES = 4 * BITS;
-    constexpr int NB = (BITS == 2) ? 2 : 1;
-    extern __shared__ __align__(16) uint8_t smem[];
+    extern __shared__ __align__(16) _Float16 lds[];
     const CacheView& V = a.v;
     const int H = V.H;
     // Work groups are dealt to the 8 XCDs in turn (block b to XCD b % 8). The
@@ -84,414 +125,501 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int s = sh / H, h = sh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, j = lane >> 4;
     const int g = a.gqa;
     const int HQ = a.num_q_heads;
 
-    // ---- the sequence and this wave's rows ----
+    // ---- the sequence ----
     const int q0 = a.cu_q[s];
     const int nq = a.cu_q[s + 1] - q0;
-    // P tokens come from the cache; with a full-precision chunk its nq tokens follow them
-    int P = a.seq_lens[s];
+    int P = a.seq_lens[s];  // tokens in the cache (before the chunk when it comes raw)
     const int slot = a.slot_ids[s];
     const bool bad = slot < 0 || slot >= V.max_seqs || P < 0;
     const bool raw_chunk = a.k_chunk != nullptr;
-    // device-side errors this wave met (wave-uniform), reported before the output
-    uint32_t err = 0;
-    if (wg == 0 && wave == 0) {
-        err = (slot < 0 || slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) | (P < 0 ? KIVI_DEVERR_LENGTH : 0u);
-        if (nq < 0 || nq > a.max_q_len || (!raw_chunk && !bad && nq > P)) err |= KIVI_DEVERR_QUERY;
+    if (wg == 0 && wave == 0) {  // device-side errors of this sequence, reported once
+        uint32_t e = (slot < 0 || slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) | (P < 0 ? KIVI_DEVERR_LENGTH : 0u);
+        if (nq < 0 || nq > a.max_q_len || (!raw_chunk && !bad && nq > P)) e |= KIVI_DEVERR_QUERY;
         if (!bad && (long long)P + (raw_chunk ? max(nq, 0) : 0) > (long long)a.bt_stride * V.Bk)
-            err |= KIVI_DEVERR_LENGTH;
-        if (err != 0 && lane == 0) report_error(V.status, err);
-        err = 0;
+            e |= KIVI_DEVERR_LENGTH;
+        if (e != 0 && lane == 0) report_error(V.status, e);
     }
     if (bad) P = 0;
     const int T = bad ? 0 : P + (raw_chunk ? nq : 0);  // tokens the rows attend over
-    const int row0 = (wg * kPWaves + wave) * kRowsPerWave;
-    if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave
-    const int TK = V.R * (P / V.R), TV = value_boundary(V, P);
-    const int n_main = TV / kTile;
-    const int tk_tiles = TK / kTile;
+    const int nrows = max(nq, 0) * g;
+    const int row0_wg = wg * kRowsWg;
+    if (row0_wg >= nrows) return;  // no rows for this work group (uniform)
     const int R = V.R;
-    const int row = row0 + n;  // this lane's row
-    const bool row_ok = row < nq * g && T > 0;
-    const int qi = row / g, qh = row % g;
-    // position of the row's query; the last visible token
-    const int my_pos = row_ok ? T - nq + qi : -1;
+    const int TK = R * (P / R), TV = value_boundary(V, P);  // quantised in the cache
+
+    // ---- this lane's row: column l % 32 of the wave's 32 rows ----
+    const int half = lane >> 5, col = lane & 31;
+    const int row = row0_wg + kRowsWave * wave + col;
+    const bool row_ok = row < nrows && T > 0;
+    const int qi = row_ok ? row / g : 0, qh = row_ok ? row % g : 0;
+    const int my_pos = T - nq + qi;
     const int my_last = row_ok ? (a.causal ? min(my_pos, T - 1) : T - 1) : -1;
-    // extent over the wave's rows (lanes of one 16-lane row hold all 16 rows)
-    int last_max = my_last, last_min = row_ok ? my_last : 0x7fffffff;
+    // extents: the work group's last visible token, the wave's smallest
+    int wave_min = row_ok ? my_last : 0x7fffffff, wave_max = my_last;
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-        last_max = max(last_max, __shfl_xor(last_max, d));
-        last_min = min(last_min, __shfl_xor(last_min, d));
+    for (int d = 1; d < 64; d <<= 1) {
+        wave_min = min(wave_min, __shfl_xor(wave_min, d));
+        wave_max = max(wave_max, __shfl_xor(wave_max, d));
     }
-    last_max = __builtin_amdgcn_readfirstlane(last_max);
-    last_min = __builtin_amdgcn_readfirstlane(last_min);
-    const int n_tiles = (last_max + 1 + kTile - 1) / kTile;  // tiles any row sees
-    const int m_end = min(n_main, n_tiles);                   // main tiles
-    const int full_tiles = (last_min + 1) / kTile;            // tiles every row sees whole
+    wave_min = __builtin_amdgcn_readfirstlane(wave_min);
+    wave_max = __builtin_amdgcn_readfirstlane(wave_max);
+    __shared__ int wg_max_sh[kPWaves];
+    if (lane == 0) wg_max_sh[wave] = wave_max;
+    __syncthreads();
+    int wg_max = wg_max_sh[0];
+#pragma unroll
+    for (int w = 1; w < kPWaves; ++w) wg_max = max(wg_max, wg_max_sh[w]);
+    const int n_tiles = wg_max >= 0 ? (wg_max + kTileTok) / kTileTok : 0;
 
-    const int tpg = 1 << a.tpg_shift, tpp = 1 << a.tpp_shift;
-    const int nch = kHeadDim * V.Bk / V.G;
-    const int meta_tile = (8 * (lane & 15) / nch) * tpp;
-    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;
-    const float sl2 = fabsf(a.scale_log2);
-    const float thr = sl2 > 0.0f ? kLazyLog2 / sl2 : 0.0f;
+    // ---- query operand: lane (col, half) holds q[row][16 ks + 8 half .. + 7] ----
+    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // scores kept as sgn q.k
+    // weight 2^(x - m), x = score * c2; a zero scale (uniform weights) is
+    // taken as the smallest normal one, so that -inf * c2 stays -inf
+    const float c2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+    h8 Qb[8];
+    {
+        const uint16_t* qrow = a.q + ((size_t)(q0 + qi) * HQ + h * g + qh) * kHeadDim + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint4 w = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : (uint4){0, 0, 0, 0};
+            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h2 p2;
+                if constexpr (DT == kBF16) {
+                    p2 = (h2){(_Float16)bf16_bits_to_f32((uint16_t)(w4[e] & 0xFFFFu)),
+                              (_Float16)bf16_bits_to_f32((uint16_t)(w4[e] >> 16))};
+                } else {
+                    p2 = as_h2(w4[e]);
+                }
+                if (sgn < 0.0f) p2 = -p2;
+                Qb[ks][2 * e] = p2[0];
+                Qb[ks][2 * e + 1] = p2[1];
+            }
+        }
+    }
 
-    uint8_t* wl = smem + wave * prefill_wave_lds_bytes();
-    uint16_t* lq = reinterpret_cast<uint16_t*>(wl);
-    uint8_t* lt = wl + kRowsPerWave * kRowBytes;
-    float* lbias = reinterpret_cast<float*>(lt + 2 * kRowsPerWave * kRowBytes);
-    const int lane_row = n * 2 * kRowBytes + 16 * j;
-    const uint32_t lane_code_off = SLOT_BYTES * lane;
-    const uint32_t lane_meta_off = 16 * NG * j;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(V.k_codes, a.code_array_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V.v_codes, a.code_array_bytes);
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(V.v_meta, a.vmeta_array_bytes);
-    const __amdgpu_buffer_rsrc_t rkm = make_rsrc(V.k_meta, a.kmeta_array_bytes);
+    // ---- the thread's part of a tile: half pt of Key slot and of Value slot
+    // L of sub-tile u. Key: channel runs r = 2 pt, 2 pt + 1 (channels
+    // 32 r + 8 j .. + 7) of token m; Value: channel tiles t = 4 pt .. 4 pt + 3
+    // (channels 16 t + m) of tokens 4 j .. 4 j + 3 ----
+    const int pt = __builtin_amdgcn_readfirstlane(tid >> 8);       // per wave
+    const int u = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // per wave
+    const int L = lane, m = L & 15, j = L >> 4;
+    const int32_t* bt = a.block_table + (size_t)s * a.bt_stride;
     const uint16_t* ringK = V.k_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
     const uint16_t* ringV = V.v_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
-    const int32_t* bt = a.block_table + (size_t)s * a.bt_stride;
-    auto page_of = [&](int t) -> int {  // block-table entry of tile t, unchecked
-        const int bi = t >> a.tpp_shift;
-        return (t < 0 || bi >= a.bt_stride) ? -1 : bt[bi];
+    // Pages per Key group (G / Bk) and the Key channels whose metadata one
+    // page holds (128 Bk / G) are powers of two: G / Bk divides 128. Bk is a
+    // multiple of 16, usually a power of two as well.
+    const int gpb_lg = __builtin_ctz((unsigned)(V.G / V.Bk));
+    const int nch_lg = __builtin_ctz((unsigned)kHeadDim) - gpb_lg, nch = 1 << nch_lg;
+    const bool bk_pow2 = (V.Bk & (V.Bk - 1)) == 0;
+    const int bk_lg = __builtin_ctz((unsigned)V.Bk);
+    auto div_bk = [&](int p) { return bk_pow2 ? p >> bk_lg : p / V.Bk; };
+    auto mod_bk = [&](int p) { return bk_pow2 ? p & (V.Bk - 1) : p % V.Bk; };
+    uint32_t err = 0;                       // pages this thread could not read
+    auto page_at = [&](int bi) -> int {     // page of table entry bi, -1 (noted) when the table has none
+        const int blk = bi < a.bt_stride ? bt[bi] : -1;
+        if (blk >= 0 && blk < V.num_blocks) return blk;
+        err |= KIVI_DEVERR_PAGE;
+        return -1;
     };
-    auto valid_pg = [&](int blk) -> int { return (blk >= 0 && blk < V.num_blocks) ? blk : -1; };
-
-    // ---- query rows to LDS (fp16), zero rows past the chunk ----
-    int my_page = page_of(lane);
-    int next_page = page_of(64 + lane);
-    {
-        uint4 qv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {  // 16 rows x 16 chunks of 8 channels
-            const int idx = lane + 64 * r, rr = idx >> 4, k = idx & 15;
-            const int rw = row0 + rr;
-            qv[r] = (uint4){0, 0, 0, 0};
-            if (rw < nq * g)
-                qv[r] = *reinterpret_cast<const uint4*>(
-                    a.q + ((size_t)(q0 + rw / g) * HQ + h * g + rw % g) * kHeadDim + 8 * k);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int idx = lane + 64 * r, rr = idx >> 4, k = idx & 15;
-            uint4 o = qv[r];
-            if constexpr (DT == kBF16) {
-                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                uint32_t cv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const _Float16 lo = (_Float16)bf16_bits_to_f32((uint16_t)(w[e] & 0xFFFFu));
-                    const _Float16 hi = (_Float16)bf16_bits_to_f32((uint16_t)(w[e] >> 16));
-                    cv[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-                }
-                o = {cv[0], cv[1], cv[2], cv[3]};
+    auto page_of = [&](int p) -> int { return page_at(div_bk(p)); };  // page of position p
+    // Key metadata of tile k, staged in LDS: thread (u, L) of the first 256
+    // loads the (scale, zero) pairs of channels 2L, 2L + 1 of sub-tile u's
+    // group (two 4-byte loads), two tiles ahead, and stores them after the
+    // current tile's computation; the restore of that tile reads them after a
+    // barrier.
+    _Float16* const meta_lds = lds + 2 * kStageHalfs;
+    auto issue_meta = [&](int k, uint32_t& ms, uint32_t& mz) {
+        ms = mz = 0;
+        const int p_sub = kTileTok * k + 16 * u;
+        if (pt == 0 && k < n_tiles && p_sub < TK) {
+            // group jg = p_sub / G; channel ch's pair sits on page jg G / Bk + ch / nch
+            const int ch = 2 * L;
+            const int blk = page_at(((div_bk(p_sub) >> gpb_lg) << gpb_lg) + (ch >> nch_lg));
+            if (blk >= 0) {
+                const uint8_t* mp = V.k_meta + ((size_t)blk * H + h) * V.k_meta_bytes + 2 * (ch & (nch - 1));
+                ms = *reinterpret_cast<const uint32_t*>(mp);
+                mz = *reinterpret_cast<const uint32_t*>(mp + 2 * nch);
             }
-            *reinterpret_cast<uint4*>(lq + rr * kQRow + 8 * k) = o;
-        }
-    }
-
-    Acc<NG, NB> st;
-    st.init();
-
-    // ---- main tiles [0, m_end): the decode pipeline, masked near the diagonal ----
-    struct Buf {
-        TileRegs<BITS, NG> t[kHalf];
-        bool ok[kHalf];
-        uint4 ms, mz;
-    };
-    int base = 0;
-    auto issue = [&](int t0, Buf& b) {
-        if (t0 - base >= 64) {
-            base += 64;
-            my_page = next_page;
-            next_page = page_of(base + 64 + lane);
-        }
-#pragma unroll
-        for (int e = 0; e < kHalf; ++e) {
-            const int t = t0 + e;
-            const int blk = valid_pg(__builtin_amdgcn_readlane(my_page, (t - base) & 63));
-            b.ok[e] = blk >= 0 && t < m_end;
-            if (blk < 0 && t < m_end) err |= KIVI_DEVERR_PAGE;
-            const uint32_t chk = (uint32_t)(b.ok[e] ? blk : 0) * (uint32_t)H + (uint32_t)h;
-            const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
-            const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
-            const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
-            if constexpr (BITS == 4) {
-                const uint4 k4 = buf_b128(rk, lane_code_off, coff);
-                const uint4 v4 = buf_b128(rv, lane_code_off, coff);
-                b.t[e].k[0] = k4.x; b.t[e].k[1] = k4.y; b.t[e].k[2] = k4.z; b.t[e].k[3] = k4.w;
-                b.t[e].v[0] = v4.x; b.t[e].v[1] = v4.y; b.t[e].v[2] = v4.z; b.t[e].v[3] = v4.w;
-            } else {
-                const uint2 k2 = buf_b64(rk, lane_code_off, coff);
-                const uint2 v2 = buf_b64(rv, lane_code_off, coff);
-                b.t[e].k[0] = k2.x; b.t[e].k[1] = k2.y;
-                b.t[e].v[0] = v2.x; b.t[e].v[1] = v2.y;
-            }
-#pragma unroll
-            for (int qd = 0; qd < NG; ++qd) {
-                const uint4 m = buf_b128(rm, lane_meta_off + 16 * qd, moff);
-                b.t[e].vm[4 * qd + 0] = m.x; b.t[e].vm[4 * qd + 1] = m.y;
-                b.t[e].vm[4 * qd + 2] = m.z; b.t[e].vm[4 * qd + 3] = m.w;
-            }
-        }
-        const int gt = ((t0 + kHalf - 1) >> a.tpg_shift) << a.tpg_shift;
-        const int mp = valid_pg(__builtin_amdgcn_ds_bpermute(4 * ((gt + meta_tile - base) & 63), my_page));
-        const uint32_t mo = k_meta_off(V, h, mp, nch);
-        b.ms = buf_b128(rkm, mo, 0);
-        b.mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
-    };
-    float bias = 0.0f;
-    auto compute = [&](const Buf& b, int t0) {
-#pragma unroll
-        for (int e = 0; e < kHalf; e += 2) {
-            const int t = t0 + e;
-            constexpr bool kPair = kHalf > 1;
-            const bool oka = b.ok[e], okb = kPair ? b.ok[kPair ? e + 1 : e] : false;
-            if (!oka && !okb) continue;
-            if ((t & (tpg - 1)) == 0 && t != 0) bias = build_table<BITS, kFoldK>(kRowsPerWave, b.ms, b.mz, lq, lt, lbias, n, sgn);
-            const TileRegs<BITS, NG>& ta = b.t[e];
-            const TileRegs<BITS, NG>& tb = b.t[kPair ? e + 1 : e];
-            f4 ra = code_scores<BITS, kFoldK>(ta.k, lt, lane_row, bias);
-            f4 rb = ra;
-            if (kPair) rb = code_scores<BITS, kFoldK>(tb.k, lt, lane_row, bias);
-            float pa[4], pb[4];
-            if (oka && okb && t + 1 < full_tiles) {  // both tiles seen whole by every row (uniform)
-                const float mx = max2(max4(ra), max4(rb));
-                st.rescale(xor_max(mx), sl2, thr);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pa[r] = st.weight(ra[r], sl2);
-                    pb[r] = st.weight(rb[r], sl2);
-                }
-            } else {
-                // visibility of token 16 t' + 4 j + r to this lane's row
-                bool va[4], vb[4];
-                const bool full_a = t < full_tiles, full_b = t + 1 < full_tiles;  // uniform
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    va[r] = oka && (full_a || 16 * t + 4 * j + r <= my_last);
-                    vb[r] = okb && (full_b || 16 * (t + 1) + 4 * j + r <= my_last);
-                }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (va[r]) mx = max2(mx, ra[r]);
-                    if (vb[r]) mx = max2(mx, rb[r]);
-                }
-                st.rescale(xor_max(mx), sl2, thr);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pa[r] = va[r] ? st.weight(ra[r], sl2) : 0.0f;
-                    pb[r] = vb[r] ? st.weight(rb[r], sl2) : 0.0f;
-                }
-            }
-            st.l_acc += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
-            value_pair<BITS, NG, NB>(st, ta.v, ta.vm, tb.v, tb.vm, pa, pb, oka, okb);
         }
     };
-    if (m_end > 0) {
-        Buf ba, bb;
-        issue(0, ba);
-        const int mp = valid_pg(__builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page));
-        const uint32_t mo = k_meta_off(V, h, mp, nch);
-        const uint4 ms0 = buf_b128(rkm, mo, 0);
-        const uint4 mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
-        bias = build_table<BITS, kFoldK>(kRowsPerWave, ms0, mz0, lq, lt, lbias, n, sgn);
-        int it = 0;
-        for (int t0 = 0; t0 < m_end; t0 += 2 * kHalf) {
-            issue(t0 + kHalf, bb);
-            compute(ba, t0);
-            if (t0 + kHalf >= m_end) break;
-            issue(t0 + 2 * kHalf, ba);
-            compute(bb, t0 + kHalf);
-            if (++it == flush_period<kHalf>()) {
-                it = 0;
-                st.template flush_offsets<BITS>();
-            }
-        }
-    }
-
-    // ---- tiles that touch the residual: [n_main, n_tiles) ----
-    for (int t = max(n_main, 0); t < n_tiles; ++t) {
-        const int tb0 = (t >> a.tpg_shift) << a.tpg_shift;
-        const int tpage = page_of(tb0 + lane);
-        const int blk = valid_pg(__builtin_amdgcn_readlane(tpage, t - tb0));
-        const int p0 = t * kTile, pq = p0 + 4 * j;
-        if (blk < 0 && (t < tk_tiles || p0 < TV)) {  // codes without a page
-            err |= KIVI_DEVERR_PAGE;
-            continue;
-        }
-        const uint32_t chk = (uint32_t)blk * (uint32_t)H + (uint32_t)h;
-        const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
-        const uint32_t coff = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
-        const uint32_t moff = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
-        f4 raw;
-        if (t < tk_tiles) {
-            uint32_t kw[BITS];
-            if constexpr (BITS == 4) {
-                const uint4 u = buf_b128(rk, lane_code_off, coff);
-                kw[0] = u.x; kw[1] = u.y; kw[2] = u.z; kw[3] = u.w;
-            } else {
-                const uint2 u = buf_b64(rk, lane_code_off, coff);
-                kw[0] = u.x; kw[1] = u.y;
-            }
-            const int mp = valid_pg(__builtin_amdgcn_ds_bpermute(4 * meta_tile, tpage));
-            const uint32_t mo = k_meta_off(V, h, mp, nch);
-            const uint4 ms = buf_b128(rkm, mo, 0);
-            const uint4 mz = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
-            const float tbias = build_table<BITS>(kRowsPerWave, ms, mz, lq, lt, lbias, n, sgn);
-            raw = code_scores<BITS>(kw, lt, lane_row, tbias);
+    auto store_meta = [&](int k, uint32_t ms, uint32_t mz) {
+        if (pt != 0) return;
+        _Float16* mt = meta_lds + (k & 1) * kMetaHalfs + u * 2 * kHeadDim;
+        *reinterpret_cast<uint32_t*>(mt + 2 * L) = ms;
+        *reinterpret_cast<uint32_t*>(mt + kHeadDim + 2 * L) = mz;
+    };
+    // the thread's code words of a sub-tile whose tokens are quantised, and the
+    // Value metadata of its 4 tokens for the groups of its channel tiles
+    constexpr int KW = BITS / 2;                 // code words per half slot
+    constexpr int NGP = NG == 1 ? 1 : NG / 2;    // Value groups per half slot
+    auto load_slot_k = [&](int blk, int p_sub, SlotRegs<BITS, NGP>& x) {
+        const uint8_t* base = V.k_codes + ((size_t)blk * H + h) * V.code_bytes +
+                              (mod_bk(p_sub) / kTile) * TILE_BYTES + SLOT_BYTES * L + 4 * KW * pt;
+        if constexpr (KW == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(base);
+            x.k[0] = w.x; x.k[1] = w.y;
         } else {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* qrow = reinterpret_cast<const uint8_t*>(lq + n * kQRow);
-            const int pk = min(p0 + n, T - 1);  // A row: token n of the tile
-            const uint16_t* krow = pk < P ? ringK + (size_t)(pk % R) * kHeadDim
-                                          : a.k_chunk + ((size_t)(q0 + pk - P) * H + h) * kHeadDim;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 kr = *reinterpret_cast<const uint4*>(krow + 32 * i + 8 * j);
-                const uint32_t ws[4] = {kr.x, kr.y, kr.z, kr.w};
-                h8 A;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) A[e] = (_Float16)to_f32<DT>((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
-                const h8 B = *reinterpret_cast<const h8*>(qrow + 2 * (32 * i + 8 * j));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
-            }
-            raw = acc * sgn;
+            x.k[0] = *reinterpret_cast<const uint32_t*>(base);
         }
-        uint32_t vw[BITS], vm[4 * NG];
-#pragma unroll
-        for (int k = 0; k < BITS; ++k) vw[k] = 0;
-#pragma unroll
-        for (int k = 0; k < 4 * NG; ++k) vm[k] = 0;
-        if (p0 < TV) {
-            if constexpr (BITS == 4) {
-                const uint4 u = buf_b128(rv, lane_code_off, coff);
-                vw[0] = u.x; vw[1] = u.y; vw[2] = u.z; vw[3] = u.w;
-            } else {
-                const uint2 u = buf_b64(rv, lane_code_off, coff);
-                vw[0] = u.x; vw[1] = u.y;
-            }
-#pragma unroll
-            for (int qd = 0; qd < NG; ++qd) {
-                const uint4 m = buf_b128(rm, lane_meta_off + 16 * qd, moff);
-                vm[4 * qd + 0] = m.x; vm[4 * qd + 1] = m.y; vm[4 * qd + 2] = m.z; vm[4 * qd + 3] = m.w;
-            }
+    };
+    auto load_slot_v = [&](int blk, int p_sub, SlotRegs<BITS, NGP>& x) {
+        const uint8_t* base = V.v_codes + ((size_t)blk * H + h) * V.code_bytes +
+                              (mod_bk(p_sub) / kTile) * TILE_BYTES + SLOT_BYTES * L + 4 * KW * pt;
+        if constexpr (KW == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(base);
+            x.v[0] = w.x; x.v[1] = w.y;
+        } else {
+            x.v[0] = *reinterpret_cast<const uint32_t*>(base);
         }
-        uint2 vr[8];
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-            vr[tt] = *reinterpret_cast<const uint2*>(ringV + vring_index(R, pq, 16 * tt + n));
-        if (raw_chunk && p0 + kTile > P) {  // chunk tokens replace their ring halves (uniform test)
-            bool inc[4];
-            const uint16_t* vrow[4];
+        // (scale, zero) of tokens 4j .. 4j + 3: all of a token's groups are one
+        // row of NG words; this half needs groups pt NG / 2 .. + NGP - 1
+        const uint8_t* mb = V.v_meta + ((size_t)blk * H + h) * V.v_meta_bytes + (size_t)(mod_bk(p_sub) + 4 * j) * NG * 4;
+        if constexpr (NG == 1) {
+            const uint4 w = *reinterpret_cast<const uint4*>(mb);
+            x.vm[0] = w.x; x.vm[1] = w.y; x.vm[2] = w.z; x.vm[3] = w.w;
+        } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                inc[r] = pq + r >= P && pq + r < T;
-                vrow[r] = a.v_chunk + ((size_t)(q0 + (inc[r] ? pq + r - P : 0)) * H + h) * kHeadDim + n;
-            }
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                uint32_t w[2] = {vr[tt].x, vr[tt].y};
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (inc[r]) {
-                        const uint32_t sh16 = 16u * (uint32_t)(r & 1);
-                        w[r >> 1] = (w[r >> 1] & ~(0xFFFFu << sh16)) | ((uint32_t)vrow[r][16 * tt] << sh16);
-                    }
-                vr[tt] = make_uint2(w[0], w[1]);
+                const uint8_t* mr = mb + (size_t)r * NG * 4 + 4 * NGP * pt;
+                if constexpr (NGP == 1) {
+                    x.vm[r] = *reinterpret_cast<const uint32_t*>(mr);
+                } else if constexpr (NGP == 2) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(mr);
+                    x.vm[2 * r] = w.x; x.vm[2 * r + 1] = w.y;
+                } else {
+                    const uint4 w = *reinterpret_cast<const uint4*>(mr);
+                    x.vm[4 * r] = w.x; x.vm[4 * r + 1] = w.y; x.vm[4 * r + 2] = w.z; x.vm[4 * r + 3] = w.w;
+                }
             }
         }
-        float p[4], mx = -INFINITY;
-        bool vis[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vis[r] = pq + r < T && pq + r <= my_last;
-            if (vis[r]) mx = max2(mx, raw[r]);
-        }
-        st.rescale(xor_max(mx), sl2, thr);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = vis[r] ? st.weight(raw[r], sl2) : 0.0f;
-        st.l_acc += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const int gg = (16 * tt) / (kHeadDim / NG);
-            const bool first_of_group = (16 * tt) % (kHeadDim / NG) == 0;
-            const uint32_t rw[2] = {vr[tt].x, vr[tt].y};
-            h4 A;
-            h8 B;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int pr = pq + r;
-                const bool is_code = pr < TV, is_raw = !is_code && pr < T;  // ring or chunk
-                const uint32_t mw = is_code ? vm[r * NG + gg] : 0u;
-                if (first_of_group) st.zacc[gg] += p[r] * f16_bits_to_f32((uint16_t)(mw >> 16));
-                const float code_v = (float)v_code_at<BITS>(vw, tt, r);
-                const float raw_v = to_f32<DT>((uint16_t)(rw[r >> 1] >> (16 * (r & 1))));
-                const float av = is_code ? code_v : (is_raw ? raw_v : 0.0f);
-                const float wv = is_code ? p[r] * f16_bits_to_f32((uint16_t)(mw & 0xFFFFu)) : (is_raw ? p[r] : 0.0f);
-                A[r] = (_Float16)av;
-                _Float16 hi, lo;
-                split_f16(wv, hi, lo);
-                B[r] = hi;
-                B[4 + r] = lo;
-            }
-            st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, st.O[tt], 0, 0, 0);
-        }
-    }
+    };
 
-    // ---- output of this wave's rows ----
-    const float l_tot = xor_sum(st.l_acc);
-    float zt[NG][NB];
+    // ---- restore into LDS ----
+    // Keys of sub-tile u, token m, the thread's 2 channel runs, from codes, with
+    // the tile's Key metadata (stage k & 1): hi = fp16(k), lo = fp16(k - hi),
+    // k = code * scale + zero; t = code * scale + zero is formed in single
+    // precision (the product is exact), and t - hi is exact before its
+    // rounding to fp16
+    auto store_k_codes = [&](_Float16* st, int k, const uint32_t* kw) {
+        const _Float16* mt = meta_lds + (k & 1) * kMetaHalfs + u * 2 * kHeadDim;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-        const float z = xor_sum(st.zacc[gg]);
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * pt + rr;
+            const uint4 sv = *reinterpret_cast<const uint4*>(mt + 32 * r + 8 * j);
+            const uint4 zv = *reinterpret_cast<const uint4*>(mt + kHeadDim + 32 * r + 8 * j);
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+            uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - (BITS == 4 ? 1024.0f * xor_sum(st.wsum[gg][vb]) : 0.0f);
+            for (int e = 0; e < 4; ++e) {
+                h2 c;
+                if constexpr (BITS == 4) c = code_pair<4>(kw[rr], 4 * e);
+                else c = code_pair<2>(kw[0], 2 * (e + 4 * rr));
+                const h2 sc = as_h2(sw[e]), zc = as_h2(zw[e]);
+                const h2 hi = __builtin_elementwise_fma(c, sc, zc);
+                h2 lo;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float t = __builtin_fmaf((float)c[q], (float)sc[q], (float)zc[q]);
+                    lo[q] = (_Float16)__builtin_fmaf((float)hi[q], -1.0f, t);
+                }
+                hw[e] = as_u32(hi);
+                lw[e] = as_u32(lo);
+            }
+            const int off = (16 * u + m) * kKRow + 32 * r + 8 * j;
+            *reinterpret_cast<uint4*>(st + off) = (uint4){hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<uint4*>(st + kKHalfs + off) = (uint4){lw[0], lw[1], lw[2], lw[3]};
+        }
+    };
+    // fp16 pair of tokens (4j + 2k, 4j + 2k + 1) of channel 16 (4 pt + tt) + m,
+    // from codes (tt = 0..3: the thread's tiles; every index below is a
+    // compile-time constant, so the registers stay registers)
+    auto v_from_codes = [&](const SlotRegs<BITS, NGP>& x, int tt, int k) -> h2 {
+        h2 c;
+        if constexpr (BITS == 4) c = code_pair<4>(x.v[tt >> 1], 4 * (2 * (tt & 1) + k));
+        else c = code_pair<2>(x.v[0], 2 * (2 * tt + k));
+        // the channel's group (Gv >= 16 > m), counted from this half's first
+        const int gg = NG == 1 ? 0 : (tt * NG) / 8;
+        const uint32_t w0 = x.vm[(2 * k) * NGP + gg], w1 = x.vm[(2 * k + 1) * NGP + gg];
+        const h2 sc = as_h2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));  // scales of the two tokens
+        const h2 zc = as_h2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));  // zero-points
+        return __builtin_elementwise_fma(c, sc, zc);
+    };
+    auto store_v = [&](_Float16* st, int t, uint32_t lo, uint32_t hi) {
+        *reinterpret_cast<uint2*>(st + kVOff + (16 * t + m) * kVRow + 16 * u + v_pos(j)) = (uint2){lo, hi};
+    };
+
+    // A tile whose 64 tokens have quantised Keys and Values, restored from
+    // registers loaded before the previous tile's computation.
+    auto fill_pure = [&](_Float16* st, int k, const SlotRegs<BITS, NGP>& x) {
+        store_k_codes(st, k, x.k);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            store_v(st, 4 * pt + tt, as_u32(v_from_codes(x, tt, 0)), as_u32(v_from_codes(x, tt, 1)));
+    };
+    // Any tile: per sub-tile (Keys; TK is a multiple of 16) and per token
+    // (Values) from codes, the residual ring, the raw chunk, or zeros past the
+    // sequence. Synchronous; only the last tiles of a sequence take it.
+    auto fill_any = [&](_Float16* st, int k) {
+        const int t0 = kTileTok * k;
+        const int p_sub = t0 + 16 * u;
+        const int blk = (p_sub < TV || p_sub < TK) ? page_of(p_sub) : -1;
+        SlotRegs<BITS, NGP> x;
+#pragma unroll
+        for (int q = 0; q < KW; ++q) x.k[q] = x.v[q] = 0;
+#pragma unroll
+        for (int q = 0; q < 4 * NGP; ++q) x.vm[q] = 0;
+        if (blk >= 0 && p_sub < TK) load_slot_k(blk, p_sub, x);
+        if (blk >= 0 && p_sub < TV) load_slot_v(blk, p_sub, x);
+        // Keys: token p = p_sub + m (full-precision values: hi = value, lo = 0)
+        const int p = p_sub + m;
+        if (p_sub < TK) {
+            store_k_codes(st, k, x.k);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = 2 * pt + rr;
+                uint4 w = {0, 0, 0, 0};
+                if (p < T) {
+                    const uint16_t* src = p < P ? ringK + (size_t)(p % R) * kHeadDim
+                                                : a.k_chunk + ((size_t)(q0 + p - P) * H + h) * kHeadDim;
+                    w = *reinterpret_cast<const uint4*>(src + 32 * r + 8 * j);
+                }
+                if constexpr (DT == kBF16) {
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = as_u32((h2){(_Float16)bf16_bits_to_f32((uint16_t)(ws[e] & 0xFFFFu)),
+                                           (_Float16)bf16_bits_to_f32((uint16_t)(ws[e] >> 16))});
+                    w = (uint4){o[0], o[1], o[2], o[3]};
+                }
+                const int off = (16 * u + m) * kKRow + 32 * r + 8 * j;
+                *reinterpret_cast<uint4*>(st + off) = w;
+                *reinterpret_cast<uint4*>(st + kKHalfs + off) = (uint4){0, 0, 0, 0};
+            }
+        }
+        // Values: tokens pv .. pv + 3, one quad of the ring (R is a multiple of 16)
+        const int pv = p_sub + 4 * j;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 4 * pt + tt;
+            const int ch = 16 * t + m;
+            uint32_t code_w[2] = {0, 0};
+            if (pv < TV) {
+                code_w[0] = as_u32(v_from_codes(x, tt, 0));
+                code_w[1] = as_u32(v_from_codes(x, tt, 1));
+            }
+            uint2 ring_w = {0, 0};
+            if (pv + 3 >= TV && pv < min(T, P)) ring_w = *reinterpret_cast<const uint2*>(ringV + vring_index(R, pv, ch));
+            uint16_t val[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pr = pv + r;
+                uint16_t bits = 0;
+                if (pr < TV) {
+                    bits = (uint16_t)(code_w[r >> 1] >> (16 * (r & 1)));
+                } else if (pr < min(T, P)) {
+                    bits = (uint16_t)((r < 2 ? ring_w.x : ring_w.y) >> (16 * (r & 1)));
+                    if constexpr (DT == kBF16) bits = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(bits));
+                } else if (pr < T) {
+                    bits = a.v_chunk[((size_t)(q0 + pr - P) * H + h) * kHeadDim + ch];
+                    if constexpr (DT == kBF16) bits = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(bits));
+                }
+                val[r] = bits;
+            }
+            store_v(st, t, (uint32_t)val[0] | ((uint32_t)val[1] << 16), (uint32_t)val[2] | ((uint32_t)val[3] << 16));
+        }
+    };
+    auto pure = [&](int k) -> bool { return kTileTok * (k + 1) <= TV && kTileTok * (k + 1) <= TK; };
+    // loads of a pure tile's codes
+    auto issue_pure = [&](int k, SlotRegs<BITS, NGP>& x) {
+        const int p_sub = kTileTok * k + 16 * u;
+        const int blk = page_of(p_sub);
+        load_slot_k(max(blk, 0), p_sub, x);
+        load_slot_v(max(blk, 0), p_sub, x);
+        if (blk < 0) {  // no page: its slot restores to zero values
+#pragma unroll
+            for (int q = 0; q < 4 * NGP; ++q) x.vm[q] = 0;
+        }
+    };
+
+    // ---- per-wave state: O^T[channel][row] in 4 blocks of 32 channels ----
+    f16v O[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) O[cb] = (f16v){};
+    float m_run = -INFINITY, l_acc = 0.0f;
+
+    // Online softmax of one 32-token block of scores (lane: row col, tokens
+    // tb0 + 8 (v / 4) + 4 half + v % 4): the block's maximum moves the running
+    // maximum (in log2 units) only when it passes it by kLazy; the weights
+    // 2^(score c2 - m) go to two fp16 B operands (k-steps 2 b, 2 b + 1).
+    // Scores of tokens past the row's last become -inf, only on blocks some
+    // row of the wave does not see whole (c2 > 0, so their weights are 0).
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    auto softmax_block = [&](f16v& S, int tb0, h8* Pb) {
+        if (tb0 + 31 > wave_min) {  // uniform
+            const int lim = my_last - tb0 - 4 * half;  // the row sees v with 8 (v / 4) + v % 4 <= lim
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (8 * (v >> 2) + (v & 3) > lim) S[v] = -INFINITY;
+        }
+        float mx = S[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mxl = mx * c2;  // -inf when the row sees none of the block
+        if (__builtin_amdgcn_ballot_w64(mxl > m_run + kLazy) != 0) {  // rare: move the running max
+            const float mnew = fmaxf(m_run, mxl);
+            const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mnew);
+            l_acc *= f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) O[cb] *= f;
+            m_run = mnew;
+        }
+        const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 8 * kk + 2 * e;
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v], c2, mneg));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v + 1], c2, mneg));
+                const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                l_acc = __builtin_amdgcn_fdot2(pp, one, l_acc, false);
+                Pb[kk][2 * e] = pp[0];
+                Pb[kk][2 * e + 1] = pp[1];
+            }
+    };
+    auto compute = [&](const _Float16* st, int t0) {
+        // S^T[token][row] for the tile's two 32-token blocks, Keys as hi + lo
+        // (the two blocks' accumulations alternate, so that no product waits
+        // for the one before it)
+        f16v S0 = (f16v){}, S1 = (f16v){};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int o0 = col * kKRow + 16 * ks + 8 * half, o1 = o0 + 32 * kKRow;
+            const h8 a0 = *reinterpret_cast<const h8*>(st + o0), a1 = *reinterpret_cast<const h8*>(st + o1);
+            const h8 b0 = *reinterpret_cast<const h8*>(st + kKHalfs + o0);
+            const h8 b1 = *reinterpret_cast<const h8*>(st + kKHalfs + o1);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, Qb[ks], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, Qb[ks], S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[ks], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[ks], S1, 0, 0, 0);
+        }
+        // block 0's softmax and PV while block 1's scores are on the matrix cores
+        const _Float16* vst = st + kVOff;
+        h8 Pb[2];
+        softmax_block(S0, t0, Pb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const h8 av = *reinterpret_cast<const h8*>(vst + (32 * cb + col) * kVRow + 16 * kk + 8 * half);
+                O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, Pb[kk], O[cb], 0, 0, 0);
+            }
+        softmax_block(S1, t0 + 32, Pb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const h8 av = *reinterpret_cast<const h8*>(vst + (32 * cb + col) * kVRow + 16 * (2 + kk) + 8 * half);
+                O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, Pb[kk], O[cb], 0, 0, 0);
+            }
+    };
+
+    // ---- the tile loop: two LDS stages, one barrier per tile ----
+    // The two halves of the work group take the iteration in opposite orders,
+    // so that on each SIMD (which runs one wave of each) one wave's matrix
+    // work meets the other's vector work. Iteration k:
+    //   first half (pt 0): loads of tile k + 1's codes and tile k + 2's Key
+    //     metadata; tile k's computation; tile k + 1's restore; the metadata
+    //     store;
+    //   second half (pt 1): tile k + 1's restore from the codes loaded in the
+    //     iteration before; the loads of tile k + 2's codes; tile k's
+    //     computation;
+    // then a barrier. A tile that is not pure is restored after the
+    // computation by both halves.
+    if (n_tiles > 0) {
+        const bool early = pt == 1;  // uniform
+        SlotRegs<BITS, (NG == 1 ? 1 : NG / 2)> nx;
+        uint32_t ms, mz;
+        issue_meta(0, ms, mz);
+        store_meta(0, ms, mz);
+        issue_meta(1, ms, mz);
+        store_meta(1, ms, mz);
+        __syncthreads();
+        if (pure(0)) {
+            issue_pure(0, nx);
+            fill_pure(lds, 0, nx);
+        } else {
+            fill_any(lds, 0);
+        }
+        if (early && n_tiles > 1 && pure(1)) issue_pure(1, nx);
+        __syncthreads();
+        for (int k = 0; k < n_tiles; ++k) {
+            _Float16* cur = lds + (k & 1) * kStageHalfs;
+            _Float16* nxt = lds + ((k + 1) & 1) * kStageHalfs;
+            const bool more = k + 1 < n_tiles;
+            const bool nxt_pure = more && pure(k + 1);
+            if (early) {
+                if (nxt_pure) fill_pure(nxt, k + 1, nx);
+                if (k + 2 < n_tiles && pure(k + 2)) issue_pure(k + 2, nx);
+            } else {
+                if (nxt_pure) issue_pure(k + 1, nx);
+                issue_meta(k + 2, ms, mz);
+            }
+            compute(cur, kTileTok * k);
+            if (!early && nxt_pure) fill_pure(nxt, k + 1, nx);
+            if (more && !nxt_pure) fill_any(nxt, k + 1);
+            if (!early) store_meta(k + 2, ms, mz);
+            __syncthreads();
+        }
     }
-    if (err != 0 && lane == 0) report_error(V.status, err);
-    if (!(row < nq * g)) return;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (err != 0) report_error(V.status, err);
+
+    // ---- output: lane (col, half) holds channels 32 cb + 8 (v / 4) + 4 half + v % 4 ----
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_acc), __float_as_uint(l_acc), false, false);
+        l_acc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (!(row < nrows)) return;
+    const float inv = l_acc > 0.0f ? 1.0f / l_acc : 0.0f;
     uint16_t* orow = a.out + ((size_t)(q0 + qi) * HQ + h * g + qh) * kHeadDim;
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int chn = 16 * tt + 4 * j + r;
-            orow[chn] = from_f32<DT>((st.O[tt][r] + zt[chn / (kHeadDim / NG)][tt % NB]) * inv);
+        for (int b = 0; b < 4; ++b) {
+            const int ch = 32 * cb + 8 * b + 4 * half;
+            const uint32_t w0 =
+                (uint32_t)from_f32<DT>(O[cb][4 * b] * inv) | ((uint32_t)from_f32<DT>(O[cb][4 * b + 1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)from_f32<DT>(O[cb][4 * b + 2] * inv) |
+                                ((uint32_t)from_f32<DT>(O[cb][4 * b + 3] * inv) << 16);
+            *reinterpret_cast<uint2*>(orow + ch) = (uint2){w0, w1};
         }
-}
-
-template <int BITS, int DT, int NG>
-void launch_pf_ng(const PrefillArgs& a, int tpg, dim3 grid, size_t lds, hipStream_t st) {
-    dim3 block(kPThreads);
-    constexpr int kMax = max_buffer_tiles_pf<NG>();
-    const int kh = std::min(kMax, tpg);
-    if (kh >= 4 && kMax >= 4)
-        hipLaunchKernelGGL((prefill_kernel<BITS, DT, NG, (kMax >= 4 ? 4 : 1)>), grid, block, lds, st, a);
-    else if (kh >= 2 && kMax >= 2)
-        hipLaunchKernelGGL((prefill_kernel<BITS, DT, NG, (kMax >= 2 ? 2 : 1)>), grid, block, lds, st, a);
-    else
-        hipLaunchKernelGGL((prefill_kernel<BITS, DT, NG, 1>), grid, block, lds, st, a);
 }
 
 template <int BITS, int DT>
-void launch_pf(const PrefillArgs& a, int ng, int tpg, dim3 grid, size_t lds, hipStream_t st) {
+void launch_pf(const PrefillArgs& a, int ng, dim3 grid, hipStream_t st) {
+    dim3 block(kPThreads);
     switch (ng) {
-        case 1: launch_pf_ng<BITS, DT, 1>(a, tpg, grid, lds, st); break;
-        case 2: launch_pf_ng<BITS, DT, 2>(a, tpg, grid, lds, st); break;
-        case 4: launch_pf_ng<BITS, DT, 4>(a, tpg, grid, lds, st); break;
-        default: launch_pf_ng<BITS, DT, 8>(a, tpg, grid, lds, st); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 1>), grid, block, kPrefillLds, st, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 2>), grid, block, kPrefillLds, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 4>), grid, block, kPrefillLds, st, a); break;
+        default: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 8>), grid, block, kPrefillLds, st, a); break;
     }
 }
 
 }  // namespace
-
-size_t prefill_lds_bytes() { return (size_t)kPWaves * prefill_wave_lds_bytes(); }
 
 int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void* q, const int32_t* cu_q,
                    int max_q_len, const int32_t* slot_ids, const int32_t* seq_lens, int max_seq_len,
@@ -513,26 +641,18 @@ int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void
     a.scale_log2 = softmax_scale * kLog2e;
     a.causal = causal;
     a.max_q_len = max_q_len;
-    const int rows = max_q_len * a.gqa;
-    const int wave_tiles = (rows + kRowsPerWave - 1) / kRowsPerWave;
-    a.wg_per_sh = (wave_tiles + kPWaves - 1) / kPWaves;
-    a.tpg_shift = __builtin_ctz((unsigned)(v.G / kTile));
-    a.tpp_shift = __builtin_ctz((unsigned)(v.Bk / kTile));
-    a.code_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.code_bytes);
-    a.vmeta_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.v_meta_bytes);
-    a.kmeta_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.k_meta_bytes);
+    const long long rows = (long long)max_q_len * a.gqa;
+    a.wg_per_sh = (int)((rows + kRowsWg - 1) / kRowsWg);
     a.out = static_cast<uint16_t*>(out);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int ng = kHeadDim / v.Gv;
-    const int tpg = v.G / kTile;
     dim3 grid((unsigned)((size_t)num_seqs * v.H * a.wg_per_sh));
-    const size_t lds = prefill_lds_bytes();
     if (v.bits == 4) {
-        if (v.dtype == kF16) launch_pf<4, kF16>(a, ng, tpg, grid, lds, st);
-        else launch_pf<4, kBF16>(a, ng, tpg, grid, lds, st);
+        if (v.dtype == kF16) launch_pf<4, kF16>(a, ng, grid, st);
+        else launch_pf<4, kBF16>(a, ng, grid, st);
     } else {
-        if (v.dtype == kF16) launch_pf<2, kF16>(a, ng, tpg, grid, lds, st);
-        else launch_pf<2, kBF16>(a, ng, tpg, grid, lds, st);
+        if (v.dtype == kF16) launch_pf<2, kF16>(a, ng, grid, st);
+        else launch_pf<2, kBF16>(a, ng, grid, st);
     }
     return (int)hipGetLastError();
 }
