@@ -45,6 +45,7 @@ namespace {
 using namespace attn;
 
 constexpr int kThreads = 512;
+constexpr int kBtPre = 1024;  // page-table entries a work group can hold in LDS
 constexpr int kWaves = 8;
 // Main tiles of a SIMD's older wave, in percent of an even split (the
 // younger wave takes 200 minus this): measured best at 130 on MI355X.
@@ -60,6 +61,11 @@ static_assert((4 * (200 - kOldShare) - kAppendShare - kFlushShare) % 2 == 0, "wa
 // subtract) and take 1024 sum_c Q'[n][c] out of the table's bias; the tail
 // tiles, whose tables are built apart, use exact codes.
 constexpr bool kFoldK = true;
+// 4-tile blocks: load buffers per wave (blocks in flight while one is
+// computed: kQuadBuffers - 1), and whether the tail tiles come first (their
+// loads overlap the first block's) or after the main range.
+constexpr int kQuadBuffers = 2;
+constexpr bool kTailFirst = false;
 // Tiles per load buffer (two buffers per wave): deeper for the lighter
 // Value metadata of wide Value groups, and never more than the tiles of a
 // Key group (so at most one group begins inside a buffer).
@@ -94,9 +100,21 @@ struct DecodeArgs {
 
 // Per-wave LDS (dynamic shared memory, one region per wave), fp16 rows of
 // kQRow elements (272 bytes: the 16-byte pad spreads rows over banks):
-//   q rows [g] | Key-group table rows [g][hi, lo] | bias [16] f32
-// The epilogue reuses the whole work group's memory for the wave merge.
-__host__ __device__ constexpr int wave_lds_bytes(int g) { return 3 * g * kRowBytes + 64; }
+//   q rows [g] | Key-group table rows [g][hi, lo] | bias [16] f32 | zero rows [hi, lo]
+// (the zero rows are the off-diagonal blocks of the 4-tile tables). The
+// epilogue reuses the whole work group's memory for the wave merge.
+__host__ __device__ constexpr int wave_lds_bytes(int g) { return 3 * g * kRowBytes + 64 + 2 * kRowBytes; }
+
+// Row rotation inside each 16-lane row (DPP row_ror).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+// Sum over the lanes n, n + 4, n + 8, n + 12 of each 16-lane row.
+__device__ __forceinline__ float quad_fold(float x) {
+    x += row_ror<4>(x);
+    return x + row_ror<8>(x);
+}
 __host__ __device__ constexpr int merge_lds_bytes(int g) { return kWaves * g * (kHeadDim + 2) * 4; }
 
 // Shared state of one work group: the sequence, the KV head, its lengths.
@@ -211,10 +229,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int H = V.H;
     const int split = blockIdx.x % a.n_splits;
     const int sh = blockIdx.x / a.n_splits;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    uint8_t* wl = smem + wave * wave_lds_bytes(a.gqa);
+    uint16_t* lq = reinterpret_cast<uint16_t*>(wl);
+    // First round trip, all at once: the sequence's length and slot, the
+    // query rows and, when it fits in LDS, the whole page-table row (then the
+    // first windows of page ids need no round trip of their own; later
+    // windows are loaded one window ahead).
+    __shared__ int bt_pre[kBtPre];
+    // (16-channel Value groups leave it out: their registers are full)
+    const bool bt_fits = NG < 8 && a.bt_stride <= kBtPre;  // uniform
+    int pre[kBtPre / kThreads];
+#pragma unroll
+    for (int e = 0; e < kBtPre / kThreads; ++e) {
+        const int idx = tid + e * kThreads;
+        pre[e] = bt_fits && idx < a.bt_stride ? a.block_table[(size_t)(sh / H) * a.bt_stride + idx] : -1;
+    }
     const WgCtx c = make_ctx(a, sh / H, sh % H);
+    load_query<DT>(a, c, lq);
+    if (bt_fits) {
+#pragma unroll
+        for (int e = 0; e < kBtPre / kThreads; ++e) bt_pre[tid + e * kThreads] = pre[e];
+        __syncthreads();
+    }
+    auto first_page = [&](int t) -> int {  // page_of_tile, from LDS when the row is there
+        if (!bt_fits) return page_of_tile(a, c, t);
+        const int bi = t >> a.tpp_shift;
+        return (t < 0 || bi >= c.bt_len) ? -1 : bt_pre[bi];
+    };
     // at least kMinSplitTiles main tiles per split when there are that many
     const int nvalid = min(a.n_splits, max(1, (c.n_main + kMinSplitTiles - 1) / kMinSplitTiles));
-    const int tid = threadIdx.x, lane = tid & 63;
     // device-side errors this wave met (wave-uniform), reported once at the end
     uint32_t err = split == 0 && tid < 64 ? c.err : 0u;
     if (split >= nvalid) {  // no work: an empty partial for the merge
@@ -223,7 +268,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 -INFINITY;
         return;
     }
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, j = lane >> 4;
     const int g = c.g;
     const int R = V.R;
@@ -285,12 +329,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int my_tail = n_tail_dealt > tail_rank ? (n_tail_dealt - tail_rank + tail_step - 1) / tail_step : 0;
     auto tail_tile = [&](int k) -> int { return c.n_main + k + ((skip_evict && c.n_main + k >= t_evict) ? 1 : 0); };
 
-    uint8_t* wl = smem + wave * wave_lds_bytes(g);
-    uint16_t* lq = reinterpret_cast<uint16_t*>(wl);
     uint8_t* lt = wl + g * kRowBytes;
     float* lbias = reinterpret_cast<float*>(lt + 2 * g * kRowBytes);
     const int nr = n < g ? n : n % g;  // padding lanes mirror a real head; their results are unused
     const int lane_row = nr * 2 * kRowBytes + 16 * j;
+    // 4-tile blocks (kHalf == 4, g in {1, 2, 4}): column n of the score and
+    // PV products is (tile n / 4 of the block, query head n % 4), and the
+    // table's B operand is block diagonal: lane (j, n) reads its head's row
+    // when j == n / 4 (the lane's k block holds tile j's channels), else the
+    // zero rows
+    constexpr bool kQuad = kHalf == 4;
+    const int nr4 = (n & 3) & (g - 1);
+    const int lane_row4 = j == (n >> 2) ? nr4 * 2 * kRowBytes : 2 * g * kRowBytes + 64;
     const uint32_t lane_code_off = SLOT_BYTES * lane;
     const uint32_t lane_meta_off = 16 * NG * j;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(V.k_codes, a.code_array_bytes);
@@ -303,12 +353,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // ---- first round trip: query rows, page ids of the first two windows
     // and of the first tail tile's Key group ----
     const int base0 = (m_begin >> a.tpg_shift) << a.tpg_shift;  // windows start on a group
-    int my_page = page_of_tile(a, c, base0 + lane);
-    int next_page = page_of_tile(a, c, base0 + 64 + lane);
+    int my_page = first_page(base0 + lane);
+    int next_page = first_page(base0 + 64 + lane);
     const int tail0 = tail_tile(tail_rank);
     const int tail_base0 = (tail0 >> a.tpg_shift) << a.tpg_shift;
-    int tail_page = my_tail > 0 ? page_of_tile(a, c, tail_base0 + lane) : -1;
-    load_query<DT>(a, c, lq);
+    int tail_page = my_tail > 0 ? first_page(tail_base0 + lane) : -1;
+    if constexpr (kQuad) {  // this wave's zero rows
+        if (lane < 2 * kRowBytes / 16)
+            *reinterpret_cast<uint4*>(lt + 2 * g * kRowBytes + 64 + 16 * lane) = (uint4){0, 0, 0, 0};
+    }
 
     Acc<NG, NB> st;
     st.init();
@@ -411,6 +464,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = (pq + r < T) ? st.weight(raw[r], sl2) : 0.0f;
         st.l_acc += (p[0] + p[1]) + (p[2] + p[3]);
+        // (16-channel Value groups keep the general path: their tail tiles
+        // already fill the registers)
+        if (NG < 8 && p0 >= TV && p0 + kTile <= T) {  // uniform: every Value token from the residual
+            h8 B;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                _Float16 hi, lo;
+                split_f16(p[r], hi, lo);
+                B[r] = hi;
+                B[4 + r] = lo;
+            }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                h4 A;
+                if constexpr (DT == kF16) {
+                    A = make_h4(x.vr[tt].x, x.vr[tt].y);
+                } else {
+                    const uint32_t rw[2] = {x.vr[tt].x, x.vr[tt].y};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) A[r] = (_Float16)to_f32<DT>((uint16_t)(rw[r >> 1] >> (16 * (r & 1))));
+                }
+                st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, st.O[tt], 0, 0, 0);
+            }
+            return;
+        }
         // Value token r: code (< TV), residual (< T) or masked, chosen by
         // selects (no divergent branches)
 #pragma unroll
@@ -529,9 +607,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // ---- second round trip: the first main buffer and the first group's
     // meta (narrow Value groups, whose tail tiles hold many registers, finish
     // the tail first; wide ones take it after the main range) ----
-    auto run_tail = [&]() {
+    // pre: the first tail tile's registers when they were loaded ahead
+    auto run_tail = [&](const TailRegs<BITS, NG>* pre) {
         for (int i = 0; i < my_tail; ++i) {
             const int t = tail_tile(tail_rank + i * tail_step);
+            if (i == 0 && pre) {
+                tail_compute(t, *pre);
+                continue;
+            }
             if (i > 0) {
                 const int tb = (t >> a.tpg_shift) << a.tpg_shift;
                 tail_page = page_of_tile(a, c, tb + lane);
@@ -542,21 +625,217 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     };
     if constexpr (NG >= 4) {
-        if (!flush_step) run_tail();
+        if (!flush_step) run_tail(nullptr);
     }
     // buffers start a multiple of kHalf tiles after the window base, so
     // window boundaries fall between buffers (tiles before m_begin may ride
     // along, not computed)
     const int t_first = m_begin - ((m_begin - base0) & (kHalf - 1));
+
+    // ---- 4-tile blocks (kQuad) ----
+    // Loads of block t0 .. t0 + 3: Value codes as in a 2-tile buffer (the
+    // lane's slot of each tile); Key codes of tile t0 + j only, all four slots
+    // (n, 0..3) of the lane's token n, so the lane holds the token's 128
+    // channels; Value metadata of tile t0 + n / 4, tokens 4j .. 4j + 3 (the
+    // lane's score column); the Key group's scales and zero-points.
+    struct Quad {
+        uint32_t k[4][BITS];  // slot jp of tile t0 + j: channels 32 i + 8 jp .. + 7 in word i (int4)
+        uint32_t v[4][BITS];  // tile t0 + e: the lane's Value slot
+        uint32_t vm[4 * NG];  // [token][group] of the lane's column tile
+        uint4 ms, mz;
+        uint32_t okm;         // bit e: tile t0 + e is computed (uniform)
+    };
+    auto issue4 = [&](int t0, Quad& b) {
+        if (t0 - base >= 64) {  // next window of page ids (loaded one window ahead)
+            base += 64;
+            my_page = next_page;
+            next_page = page_of_tile(a, c, base + 64 + lane);
+        }
+        uint32_t coff[4], moff[4], okm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + e;
+            const int blk = valid_page(a, __builtin_amdgcn_readlane(my_page, (t - base) & 63));
+            const bool mine = t >= m_begin && t < m_end;
+            const bool ok = blk >= 0 && mine;
+            if (blk < 0 && mine) err |= KIVI_DEVERR_PAGE;
+            okm |= ok ? 1u << e : 0u;
+            const uint32_t chk = (uint32_t)(ok ? blk : 0) * (uint32_t)H + (uint32_t)c.h;
+            const uint32_t sub = (uint32_t)t & ((1u << a.tpp_shift) - 1u);
+            coff[e] = chk * (uint32_t)V.code_bytes + sub * TILE_BYTES;
+            moff[e] = chk * (uint32_t)V.v_meta_bytes + sub * (kTile * NG * 4);
+            if constexpr (BITS == 4) {
+                const uint4 u = buf_b128(rv, lane_code_off, coff[e]);
+                b.v[e][0] = u.x; b.v[e][1] = u.y; b.v[e][2] = u.z; b.v[e][3] = u.w;
+            } else {
+                const uint2 u = buf_b64(rv, lane_code_off, coff[e]);
+                b.v[e][0] = u.x; b.v[e][1] = u.y;
+            }
+        }
+        b.okm = okm;
+        const uint32_t kc = j == 0 ? coff[0] : j == 1 ? coff[1] : j == 2 ? coff[2] : coff[3];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            const uint32_t vo = kc + (uint32_t)(SLOT_BYTES * (n + 16 * jp));
+            if constexpr (BITS == 4) {
+                const uint4 u = buf_b128(rk, vo, 0);
+                b.k[jp][0] = u.x; b.k[jp][1] = u.y; b.k[jp][2] = u.z; b.k[jp][3] = u.w;
+            } else {
+                const uint2 u = buf_b64(rk, vo, 0);
+                b.k[jp][0] = u.x; b.k[jp][1] = u.y;
+            }
+        }
+        const int tn = n >> 2;
+        const uint32_t mo = (tn == 0 ? moff[0] : tn == 1 ? moff[1] : tn == 2 ? moff[2] : moff[3]) + lane_meta_off;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const uint4 m = buf_b128(rm, mo + 16 * q, 0);
+            b.vm[4 * q + 0] = m.x; b.vm[4 * q + 1] = m.y; b.vm[4 * q + 2] = m.z; b.vm[4 * q + 3] = m.w;
+        }
+        // the Key group of the block (blocks never straddle a group)
+        const int gt = (t0 >> a.tpg_shift) << a.tpg_shift;
+        const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * ((gt + meta_tile - base) & 63), my_page));
+        const uint32_t mko = k_meta_off(V, c.h, mp, nch);
+        b.ms = buf_b128(rkm, mko, 0);
+        b.mz = buf_b128(rkm, mko + 2u * (uint32_t)nch, 0);
+    };
+    const uint32_t diag_w[4] = {(n >> 2) == 0 ? ~0u : 0u, (n >> 2) == 1 ? ~0u : 0u, (n >> 2) == 2 ? ~0u : 0u,
+                                (n >> 2) == 3 ? ~0u : 0u};
+    auto diag = [&](uint32_t w) -> h8 {  // w in the dword of the lane's column tile, zeros elsewhere
+        return make_h8(w & diag_w[0], w & diag_w[1], w & diag_w[2], w & diag_w[3]);
+    };
+    auto compute4 = [&](const Quad& b, int t0) {
+        if ((t0 & (tpg - 1)) == 0 && t0 != t_first)
+            bias = build_table<BITS, kFoldK>(g, b.ms, b.mz, lq, lt, lbias, nr4, sgn);
+        const bool okc = (b.okm >> (n >> 2)) & 1u;
+        // scores of column (tile n / 4, head n % 4), tokens 4j .. 4j + 3:
+        // one k-step per 8 channels (k = 8 tile + e), two chains (table hi, lo)
+        f4 sh = {bias, bias, bias, bias}, sl = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t* trow = lt + lane_row4;
+#pragma unroll
+        for (int c8 = 0; c8 < 16; ++c8) {
+            const int jp = c8 & 3, i = c8 >> 2;
+            h8 A;
+            if constexpr (BITS == 4) {
+                const uint32_t w = b.k[jp][i], w8 = w >> 8;
+                A = make_h8(magic_pair(w, 0x000F000Fu), magic_pair(w, 0x00F000F0u), magic_pair(w8, 0x000F000Fu),
+                            magic_pair(w8, 0x00F000F0u));
+            } else {
+                const uint32_t x = b.k[jp][i >> 1], xs = (i & 1) ? x >> 8 : x;
+                A = make_h8(magic_pair(xs, 0x00030003u), magic_pair(xs, 0x000C000Cu), magic_pair(xs, 0x00300030u),
+                            magic_pair(xs, 0x00C000C0u));
+            }
+            const h8 bh = *reinterpret_cast<const h8*>(trow + 16 * c8);
+            const h8 bl = *reinterpret_cast<const h8*>(trow + kRowBytes + 16 * c8);
+            sh = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, sh, 0, 0, 0);
+            sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, sl, 0, 0, 0);
+        }
+        const f4 raw = sh + sl;
+        // the head's largest score over the block: lanes n + 16 r, and the
+        // four tiles n % 4 + 4 e
+        float mx = okc ? max4(raw) : -INFINITY;
+        mx = xor_max(mx);
+        mx = max2(mx, row_ror<4>(mx));
+        mx = max2(mx, row_ror<8>(mx));
+        st.rescale(mx, sl2, thr);
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = okc ? st.weight(raw[r], sl2) : 0.0f;
+        const h2 pp01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+        const h2 pp23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+        const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        st.l_acc = __builtin_amdgcn_fdot2(pp23, one, __builtin_amdgcn_fdot2(pp01, one, st.l_acc, false), false);
+        // Value weights W = p * scale / F (F: the place value of tokens 2, 3's
+        // fields), zero-point sums, and the PV B operands (the lane's dword of
+        // k-step h holds its tokens 2h, 2h + 1)
+        constexpr float kF23 = (BITS == 4) ? 0.0625f : 0.25f;
+        const h2 f23 = {(_Float16)kF23, (_Float16)kF23};
+        h8 Bq[NG][NB][2];
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            const uint32_t m0 = okc ? b.vm[0 * NG + gg] : 0u, m1 = okc ? b.vm[1 * NG + gg] : 0u;
+            const uint32_t m2 = okc ? b.vm[2 * NG + gg] : 0u, m3 = okc ? b.vm[3 * NG + gg] : 0u;
+            const h2 w01 = pp01 * __builtin_bit_cast(h2, lo_halves(m0, m1));
+            const h2 w23 = (pp23 * f23) * __builtin_bit_cast(h2, lo_halves(m2, m3));
+            float z = __builtin_amdgcn_fdot2(pp01, __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x07060302u)),
+                                             st.zacc[gg], false);
+            st.zacc[gg] = __builtin_amdgcn_fdot2(pp23, __builtin_bit_cast(h2, __builtin_amdgcn_perm(m3, m2, 0x07060302u)),
+                                                 z, false);
+            if constexpr (BITS == 4) {
+                st.wsum[gg][0] =
+                    __builtin_amdgcn_fdot2(w23, one, __builtin_amdgcn_fdot2(w01, one, st.wsum[gg][0], false), false);
+            }
+            Bq[gg][0][0] = diag(__builtin_bit_cast(uint32_t, w01));
+            Bq[gg][0][1] = diag(__builtin_bit_cast(uint32_t, w23));
+            if constexpr (NB == 2) {  // odd channel tiles: fields 4 places up (factor 1/16)
+                const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+                Bq[gg][NB - 1][0] = diag(__builtin_bit_cast(uint32_t, w01 * k16));
+                Bq[gg][NB - 1][1] = diag(__builtin_bit_cast(uint32_t, w23 * k16));
+            }
+        }
+        // PV: channel tile tt, k-step h: k = 8 jj + 2 e + q holds tile e's
+        // token 4 jj + 2 h + q (jj: the lane's k block)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const int gg = (16 * tt) / (kHeadDim / NG);
+            uint32_t a0[4], a1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (BITS == 4) {
+                    const uint32_t w = b.v[e][tt >> 1], ws = (tt & 1) ? w >> 8 : w;
+                    a0[e] = magic_pair(ws, 0x000F000Fu);
+                    a1[e] = magic_pair(ws, 0x00F000F0u);
+                } else {
+                    const uint32_t x = b.v[e][tt >> 2], xs = (tt & 2) ? x >> 8 : x;
+                    a0[e] = exact_pair(xs, (tt & 1) ? 0x00300030u : 0x00030003u);
+                    a1[e] = exact_pair(xs, (tt & 1) ? 0x00C000C0u : 0x000C000Cu);
+                }
+            }
+            st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(make_h8(a0[0], a0[1], a0[2], a0[3]),
+                                                              Bq[gg][tt % NB][0], st.O[tt], 0, 0, 0);
+            st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(make_h8(a1[0], a1[1], a1[2], a1[3]),
+                                                              Bq[gg][tt % NB][1], st.O[tt], 0, 0, 0);
+        }
+    };
+    // back to one column per query head: sums over the block's four tiles
+    auto quad_to_heads = [&]() {
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.O[tt][r] = quad_fold(st.O[tt][r]);
+        st.l_acc = quad_fold(st.l_acc);
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            st.zacc[gg] = quad_fold(st.zacc[gg]);
+#pragma unroll
+            for (int vb = 0; vb < NB; ++vb) st.wsum[gg][vb] = quad_fold(st.wsum[gg][vb]);
+        }
+    };
+
     Buf ba, bb;
+    Quad qa, qb;
     uint4 ms0 = {0, 0, 0, 0}, mz0 = {0, 0, 0, 0};
     if (m_begin < m_end) {
-        issue(t_first, ba);
-        const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page));
-        const uint32_t mo = k_meta_off(V, c.h, mp, nch);
-        ms0 = buf_b128(rkm, mo, 0);
-        mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+        if constexpr (kQuad) {
+            issue4(t_first, qa);
+        } else {
+            issue(t_first, ba);
+            const int mp = valid_page(a, __builtin_amdgcn_ds_bpermute(4 * meta_tile, my_page));
+            const uint32_t mo = k_meta_off(V, c.h, mp, nch);
+            ms0 = buf_b128(rkm, mo, 0);
+            mz0 = buf_b128(rkm, mo + 2u * (uint32_t)nch, 0);
+        }
     }
+    // the tile of the Value token that leaves the window, taken by the wave
+    // that wrote it (its own stores complete first)
+    auto evict_tile = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+        const int tb = (t_evict >> a.tpg_shift) << a.tpg_shift;
+        const int tpage = page_of_tile(a, c, tb + lane);
+        TailRegs<BITS, NG> x;
+        tail_issue(t_evict, tpage, x);
+        tail_compute(t_evict, x);
+    };
     // Fused step: split 0 appends this step's token with three waves while the
     // others stream (wave 7: Value eviction and residual writes; waves 5 and 6:
     // the Key flush when the residual fills). Main tiles lie below the old
@@ -564,14 +843,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     if (a.fuse && split == 0) {
         if (wave == kWaves - 1) {
             append_token_value_wave<BITS, DT>(a.app, c.s, c.h, lane);
-            if (skip_evict) {  // the tile it just wrote: its own stores complete first
-                __builtin_amdgcn_s_waitcnt(0);
-                const int tb = (t_evict >> a.tpg_shift) << a.tpg_shift;
-                const int tpage = page_of_tile(a, c, tb + lane);
-                TailRegs<BITS, NG> x;
-                tail_issue(t_evict, tpage, x);
-                tail_compute(t_evict, x);
-            }
+            if (!kQuad && skip_evict) evict_tile();  // 4-tile blocks: after the main range
         } else if (wave >= kWaves - 3) {
             // the flush is on the step's critical path: the flush waves, younger
             // than the streaming wave on their SIMD, take issue priority for it
@@ -580,7 +852,63 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             __builtin_amdgcn_s_setprio(0);
         }
     }
-    if (m_begin < m_end) {
+    if constexpr (kQuad) {
+        // tail tiles first (per-head columns), then the state moves to the
+        // block columns: lanes n >= 4 clear their sums, so that the fold over
+        // the four tiles counts the tail once (a flush step reads its tail
+        // only after the flush)
+        if (kTailFirst && !flush_step) {
+            run_tail(nullptr);
+            if (n >= 4) {
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) st.O[tt] = (f4){0.f, 0.f, 0.f, 0.f};
+                st.l_acc = 0.0f;
+#pragma unroll
+                for (int gg = 0; gg < NG; ++gg) {
+                    st.zacc[gg] = 0.0f;
+#pragma unroll
+                    for (int vb = 0; vb < NB; ++vb) st.wsum[gg][vb] = 0.0f;
+                }
+            }
+        }
+        if (m_begin < m_end) {
+            bias = build_table<BITS, kFoldK>(g, qa.ms, qa.mz, lq, lt, lbias, nr4, sgn);
+            int it = 0;
+            if constexpr (kQuadBuffers == 3) {
+                Quad qc;
+                issue4(t_first + 4, qb);
+                for (int t0 = t_first; t0 < m_end; t0 += 12) {
+                    issue4(t0 + 8, qc);
+                    compute4(qa, t0);
+                    if (t0 + 4 >= m_end) break;
+                    issue4(t0 + 12, qa);
+                    compute4(qb, t0 + 4);
+                    if (t0 + 8 >= m_end) break;
+                    issue4(t0 + 16, qb);
+                    compute4(qc, t0 + 8);
+                    if (++it == 3) {
+                        it = 0;
+                        st.template flush_offsets<BITS>();
+                    }
+                }
+            } else {
+                for (int t0 = t_first; t0 < m_end; t0 += 8) {
+                    issue4(t0 + 4, qb);
+                    compute4(qa, t0);
+                    if (t0 + 4 >= m_end) break;
+                    issue4(t0 + 8, qa);
+                    compute4(qb, t0 + 4);
+                    if (++it == flush_period<kHalf>()) {
+                        it = 0;
+                        st.template flush_offsets<BITS>();
+                    }
+                }
+            }
+        }
+        quad_to_heads();
+        if (a.fuse && split == 0 && wave == kWaves - 1 && skip_evict) evict_tile();
+        if (!kTailFirst && !flush_step) run_tail(nullptr);
+    } else if (m_begin < m_end) {
         bias = build_table<BITS, kFoldK>(g, ms0, mz0, lq, lt, lbias, nr, sgn);
         int it = 0;
         for (int t0 = t_first; t0 < m_end; t0 += 2 * kHalf) {
@@ -600,15 +928,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // wave starts streaming at once (a fused step gained 1.4 us per call).
     // The tail reads nothing this launch
     // writes but the evicted token's tile, which stays with the appending wave.
-    if constexpr (NG < 4) {
-        if (!flush_step) run_tail();
+    if constexpr (NG < 4 && !kQuad) {
+        if (!flush_step) run_tail(nullptr);
     }
     if (flush_step) {
         // the append's stores complete, then split 0 takes the tail tiles,
         // which hold what it wrote (the step's own token comes from its row)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        run_tail();
+        run_tail(nullptr);
     }
     // ---------------- merge the waves in LDS ----------------
     {
@@ -710,8 +1038,11 @@ void launch_ng(const DecodeArgs& a, int tpg, dim3 grid, size_t lds, hipStream_t 
     dim3 block(kThreads);
     constexpr int kMax = max_buffer_tiles<NG>();
     const int kh = std::min(kMax, tpg);
-    if (kh >= 4 && kMax >= 4)
-        hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, (kMax >= 4 ? 4 : 1)>), grid, block, lds, st, a);
+    // 4-tile blocks: at most 4 query heads per KV head (a power of two), Key
+    // groups of 4 tiles or more, Value groups of 64 channels or more
+    const bool quad = tpg >= 4 && (a.gqa == 1 || a.gqa == 2 || a.gqa == 4);
+    if (NG <= 2 && quad)
+        hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, (NG <= 2 ? 4 : 1)>), grid, block, lds, st, a);
     else if (kh >= 2 && kMax >= 2)
         hipLaunchKernelGGL((decode_kernel<BITS, DT, NG, (kMax >= 2 ? 2 : 1)>), grid, block, lds, st, a);
     else
