@@ -229,3 +229,22 @@ def test_decode_large_pages(bits):
     got = gc.decode(q, SCALE)
     ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False, threads=8)
     check_attention(got, ref, w.dtype, label="64-token pages")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_two_heads_per_kv_head_wide_value_groups(bits):
+    """2 query heads per KV head (4-tile blocks with mirrored head columns) and 64-channel
+    Value groups (two per token); one request longer than 16384 tokens, so its page-table
+    row (1063 entries) is too long to be held in LDS and its first windows come from memory."""
+    w = _variant(2, bits=bits, num_kv_heads=2, num_q_heads=4, v_group=64, num_seqs=3,
+                 seq_lens=[17000, 2000, 50], shuffle=True, pool_factor=1.2)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*[w.kv_stream(s) for s in range(w.num_seqs)])
+    gc.append(list(rk), list(rv))
+    assert gc.bt_np.shape[1] > 1024
+    q = w.q_decode(3)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False,
+                               threads=8)
+    check_attention(got, ref, w.dtype, label=f"g 2, Gv 64, int{bits}")

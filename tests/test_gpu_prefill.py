@@ -103,3 +103,22 @@ def test_prefill_large_pages():
     w = inputs.config(5, num_seqs=2, seq_lens=[900, 333], extra_tokens=100, block_size=64, shuffle=True,
                       pool_factor=1.5)
     _prefill_case(w, [100, 100], causal=True)
+
+
+def test_prefill_one_subtile_key_groups_narrow_value_groups():
+    """G = 16 (each 16-token sub-tile of a 64-token tile has its own Key scales)
+    and Gv = 16 (8 Value groups per token), fp16, R = 32, with the chunk spilling
+    past the residual."""
+    w = inputs.config(2, num_seqs=3, num_kv_heads=2, num_q_heads=8, k_group=16, v_group=16, residual=32,
+                      seq_lens=[213, 64, 5], extra_tokens=70, shuffle=True, pool_factor=1.5)
+    _prefill_case(w, [70, 33, 70], causal=True)
+
+
+def test_prefill_widest_key_groups_int2_32_token_pages():
+    """G = 256 over 32-token pages (8 pages per Key group), Gv = 64, int2, bf16,
+    non-causal and causal."""
+    w = inputs.config(5, bits=2, num_seqs=2, num_kv_heads=2, num_q_heads=6, k_group=256, v_group=64,
+                      residual=256, block_size=32, seq_lens=[1100, 300], extra_tokens=120, shuffle=True,
+                      pool_factor=1.5)
+    _prefill_case(w, [120, 57], causal=True)
+    _prefill_case(w, [120, 57], causal=False)
