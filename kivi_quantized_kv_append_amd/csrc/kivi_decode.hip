@@ -741,8 +741,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = okc ? st.weight(raw[r], sl2) : 0.0f;
-        const h2 pp01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
-        const h2 pp23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+        const h2 pp01 = {(_Float16)p[0], (_Float16)p[1]};  // round to nearest (one v_cvt_pk_f16_f32)
+        const h2 pp23 = {(_Float16)p[2], (_Float16)p[3]};
         const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
         st.l_acc = __builtin_amdgcn_fdot2(pp23, one, __builtin_amdgcn_fdot2(pp01, one, st.l_acc, false), false);
         // Value weights W = p * scale / F (F: the place value of tokens 2, 3's

@@ -459,7 +459,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     // Online softmax of one 32-token block of scores (lane: row col, tokens
     // tb0 + 8 (v / 4) + 4 half + v % 4): the block's maximum moves the running
     // maximum (in log2 units) only when it passes it by kLazy; the weights
-    // 2^(score c2 - m) go to two fp16 B operands (k-steps 2 b, 2 b + 1).
+    // 2^(score c2 - m) go to two fp16 B operands (k-steps 2 b, 2 b + 1),
+    // rounded to nearest.
     // Scores of tokens past the row's last become -inf, only on blocks some
     // row of the wave does not see whole (c2 > 0, so their weights are 0).
     const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
                 const int v = 8 * kk + 2 * e;
                 const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v], c2, mneg));
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[v + 1], c2, mneg));
-                const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                const h2 pp = {(_Float16)p0, (_Float16)p1};  // round to nearest (one v_cvt_pk_f16_f32)
                 l_acc = __builtin_amdgcn_fdot2(pp, one, l_acc, false);
                 Pb[kk][2 * e] = pp[0];
                 Pb[kk][2 * e + 1] = pp[1];
