@@ -31,8 +31,6 @@ namespace {
 
 using namespace attn;
 
-constexpr int kF8Threads = 256;  // prefill work groups: 4 waves
-constexpr int kF8Waves = 4;
 constexpr int kF8DecWaves = 8;  // decode work groups: 8 waves (4 waves measured ~4 % slower, 16 no faster)
 constexpr int kF8DecThreads = 64 * kF8DecWaves;
 constexpr int kF8TileBytes = kTile * kHeadDim;  // 2 KiB: 64 lane slots of 32 bytes
@@ -398,208 +396,6 @@ __global__ __launch_bounds__(kHeadDim) void fp8_merge_kernel(const float* partia
 
 // ---------------------------------------------------------------- prefill ---
 //
-// Chunked prefill over the FP8 cache ("4.4 KV Cache 量化", sections 2 and 4):
-// the rows of a request's chunk are (query token i, query head of the GQA
-// group), token-major; each wave owns 16 consecutive rows of one (request, KV
-// head), which are the MFMA N dimension in place of decode's query heads, and
-// walks the tiles up to its last row's horizon with a per-row mask. No split:
-// each row's softmax state is complete in its wave.
-
-constexpr int kF8Rows = 16;  // rows per wave
-
-struct F8PrefillArgs {
-    const uint8_t* k_codes;
-    const uint8_t* v_codes;
-    uint32_t* status;  // kivi_device_error bits
-    int max_q_len;     // the caller's bound of every query span
-    int H, Bk, num_blocks, per_head;
-    uint32_t code_bytes, code_array_bytes;
-    const uint16_t* q;
-    const int32_t* cu_q;
-    const int32_t* seq_lens;
-    const float* k_scale;
-    const float* v_scale;
-    const int32_t* block_table;
-    int bt_stride;
-    int num_q_heads, gqa, wg_per_sh, causal;
-    float scale_log2;
-    uint16_t* out;
-};
-
-template <int DT>
-__global__ __launch_bounds__(kF8Threads, 2) void fp8_prefill_kernel(F8PrefillArgs a) {
-    // work groups are dealt to the 8 XCDs in turn; the blocks of one XCD take
-    // consecutive work items, so the work groups of one (request, KV head)
-    // share that XCD's L2
-    constexpr int kXcds = 8;
-    const int nblk = (int)gridDim.x, xcd = (int)blockIdx.x % kXcds, per = nblk / kXcds, extra = nblk % kXcds;
-    const int item = xcd * per + min(xcd, extra) + (int)blockIdx.x / kXcds;
-    const int wg = item % a.wg_per_sh, sh = item / a.wg_per_sh;
-    const int s = sh / a.H, h = sh % a.H;
-    const int g = a.gqa, HQ = a.num_q_heads;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15, j = lane >> 4;
-    const int q0 = a.cu_q[s], nq = a.cu_q[s + 1] - q0;
-    const int T = max(a.seq_lens[s], 0);
-    if (wg == 0 && wave == 0) {  // the sequence's lengths, checked once
-        uint32_t e = a.seq_lens[s] < 0 || (long long)T > (long long)a.bt_stride * a.Bk ? KIVI_DEVERR_LENGTH : 0u;
-        if (nq < 0 || nq > a.max_q_len || nq > T) e |= KIVI_DEVERR_QUERY;
-        if (e != 0 && lane == 0) report_error(a.status, e);
-    }
-    const int row0 = (wg * kF8Waves + wave) * kF8Rows;
-    if (nq <= 0 || row0 >= nq * g) return;  // no rows for this wave (uniform)
-    uint32_t err = 0;  // pages this wave could not read (wave-uniform)
-    // this lane's row (one of 16 per wave; the 4 lanes n, n+16, ... share it)
-    const int row = row0 + n;
-    const bool row_ok = row < nq * g;
-    const int qi = row_ok ? row / g : 0, hh = row_ok ? row % g : 0;
-    const int pos = T - nq + qi;  // the row's position
-    const int last = row_ok ? (a.causal ? min(pos, T - 1) : T - 1) : -1;  // last visible token (-1: none)
-    int last_max = last;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) last_max = max(last_max, __shfl_xor(last_max, d));
-    last_max = __builtin_amdgcn_readfirstlane(last_max);
-    const int n_tiles = last_max >= 0 ? (last_max + kTile) / kTile : 0;
-
-    const float ks = a.k_scale[a.per_head ? h : 0];
-    const float vs = a.v_scale[a.per_head ? h : 0];
-    const float xs = a.scale_log2 * ks * 256.0f;
-
-    // query operand: lane (n, j) holds row n's q[32 i + 8 j .. + 7], i = 0..3
-    h8 Bq[4];
-    {
-        const uint16_t* qrow = a.q + ((size_t)(q0 + qi) * HQ + h * g + hh) * kHeadDim + 8 * j;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * i);
-            if (!row_ok) u = (uint4){0, 0, 0, 0};
-            if constexpr (DT == kBF16) {
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const _Float16 lo = (_Float16)bf16_bits_to_f32((uint16_t)(w[e] & 0xFFFFu));
-                    const _Float16 hi = (_Float16)bf16_bits_to_f32((uint16_t)(w[e] >> 16));
-                    o[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-                }
-                u = (uint4){o[0], o[1], o[2], o[3]};
-            }
-            Bq[i] = make_h8(u.x, u.y, u.z, u.w);
-        }
-    }
-
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_codes, a.code_array_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_codes, a.code_array_bytes);
-    const int32_t* bt = a.block_table + (size_t)s * a.bt_stride;
-    const int tpp_shift = __builtin_ctz((unsigned)(a.Bk / kTile));
-    auto page_ids = [&](int t0) -> int {  // lane l: page of tile t0 + l (-1 past the range or the table)
-        const int bi = (t0 + lane) >> tpp_shift;
-        return (t0 + lane < n_tiles && bi < a.bt_stride) ? bt[bi] : -1;
-    };
-    int base = 0;
-    int my_page = page_ids(0);
-    int next_page = page_ids(64);
-    const uint32_t lane_off = 32u * (uint32_t)lane;
-    auto issue = [&](int t, F8Tile& x) {
-        if (t - base >= 64) {
-            base += 64;
-            my_page = next_page;
-            next_page = page_ids(base + 64);
-        }
-        const int pg = __builtin_amdgcn_readlane(my_page, (t - base) & 63);
-        x.ok = t < n_tiles && pg >= 0 && pg < a.num_blocks;
-        if (t < n_tiles && !x.ok) err |= KIVI_DEVERR_PAGE;
-        const uint32_t off = ((uint32_t)(x.ok ? pg : 0) * (uint32_t)a.H + (uint32_t)h) * a.code_bytes +
-                             (uint32_t)(t & ((1 << tpp_shift) - 1)) * kF8TileBytes;
-        x.k[0] = buf_b128(rk, lane_off, off);
-        x.k[1] = buf_b128(rk, lane_off + 16u, off);
-        x.v[0] = buf_b128(rv, lane_off, off);
-        x.v[1] = buf_b128(rv, lane_off + 16u, off);
-    };
-
-    float m_run = -INFINITY, l_acc = 0.0f;
-    f4 O[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) O[t] = (f4){0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const F8Tile& x, int t) {
-        if (!x.ok) return;
-        const uint32_t kw[8] = {x.k[0].x, x.k[0].y, x.k[0].z, x.k[0].w, x.k[1].x, x.k[1].y, x.k[1].z, x.k[1].w};
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const h8 A = make_h8(f8_pair<false>(kw[2 * i]), f8_pair<true>(kw[2 * i]),
-                                 f8_pair<false>(kw[2 * i + 1]), f8_pair<true>(kw[2 * i + 1]));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[i], acc, 0, 0, 0);
-        }
-        // acc[r]: token 16 t + 4 j + r, row n; tokens past the row's last are masked
-        const int p0 = kTile * t + 4 * j;
-        float xr[4], mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            xr[r] = p0 + r <= last ? acc[r] * xs : -INFINITY;
-            mx = fmaxf(mx, xr[r]);
-        }
-        // lazy running max as in decode; a row may see no token of this tile
-        // (its max stays -inf and its weights 0)
-        const float mt = xor_max(mx);
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazyLog2) != 0) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_acc *= alpha;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) O[tt] *= alpha;
-            m_run = m_new;
-        }
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = xr[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(xr[r] - m_run);
-        l_acc += (p[0] + p[1]) + (p[2] + p[3]);
-        h8 B;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            _Float16 hi, lo;
-            split_f16(p[r], hi, lo);
-            B[r] = hi;
-            B[4 + r] = lo;
-        }
-        uint32_t vw[8] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w, x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
-        if (kTile * t + kTile > T) mask_past_end(vw, p0, T);
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const h4 A = make_h4(f8_pair<false>(vw[tt]), f8_pair<true>(vw[tt]));
-            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dup_h8(A), B, O[tt], 0, 0, 0);
-        }
-    };
-
-    if (n_tiles > 0) {
-        F8Tile xa, xb;
-        issue(0, xa);
-        for (int t = 0; t < n_tiles; t += 2) {
-            issue(t + 1, xb);
-            compute(xa, t);
-            if (t + 1 >= n_tiles) break;
-            issue(t + 2, xa);
-            compute(xb, t + 1);
-        }
-    }
-
-    // the row's output: lane (n, j) holds channels 16 tt + 4 j + r
-    const float l_tot = xor_sum(l_acc);
-    if (err != 0 && lane == 0) report_error(a.status, err);
-    if (!row_ok) return;
-    const float f = l_tot > 0.0f ? vs * 256.0f / l_tot : 0.0f;
-    uint16_t* orow = a.out + ((size_t)(q0 + qi) * HQ + h * g + hh) * kHeadDim + 4 * j;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-        const uint32_t w0 = (uint32_t)from_f32<DT>(O[tt][0] * f) | ((uint32_t)from_f32<DT>(O[tt][1] * f) << 16);
-        const uint32_t w1 = (uint32_t)from_f32<DT>(O[tt][2] * f) | ((uint32_t)from_f32<DT>(O[tt][3] * f) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * tt) = (uint2){w0, w1};
-    }
-}
-
 }  // namespace
 
 Fp8Plan fp8_decode_plan(int num_seqs, int num_kv_heads, int num_q_heads, int max_seq_len) {
@@ -685,46 +481,6 @@ int launch_fp8_decode(const CacheView& v, int per_head, int num_seqs, int num_q_
             hipLaunchKernelGGL((fp8_merge_kernel<kBF16>), mgrid, dim3(kHeadDim), 0, st, partials, plan.n_splits,
                                a.out);
     }
-    return (int)hipGetLastError();
-}
-
-}  // namespace kivi
-
-namespace kivi {
-
-int launch_fp8_prefill(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
-                       const int32_t* cu_q, int max_q_len, const int32_t* seq_lens, const float* k_scale,
-                       const float* v_scale, const int32_t* block_table, int bt_stride, float softmax_scale,
-                       int causal, void* out, void* stream) {
-    F8PrefillArgs a;
-    a.k_codes = v.k_codes;
-    a.v_codes = v.v_codes;
-    a.status = v.status;
-    a.max_q_len = max_q_len;
-    a.H = v.H;
-    a.Bk = v.Bk;
-    a.num_blocks = v.num_blocks;
-    a.per_head = per_head;
-    a.code_bytes = (uint32_t)v.code_bytes;
-    a.code_array_bytes = (uint32_t)((uint64_t)v.num_blocks * v.H * v.code_bytes);
-    a.q = static_cast<const uint16_t*>(q);
-    a.cu_q = cu_q;
-    a.seq_lens = seq_lens;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.bt_stride = bt_stride;
-    a.num_q_heads = num_q_heads;
-    a.gqa = num_q_heads / v.H;
-    a.causal = causal;
-    a.scale_log2 = softmax_scale * kLog2e;
-    a.out = static_cast<uint16_t*>(out);
-    const int rows_per_wg = kF8Waves * kF8Rows;
-    a.wg_per_sh = (max_q_len * a.gqa + rows_per_wg - 1) / rows_per_wg;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    dim3 grid((unsigned)((size_t)num_seqs * v.H * a.wg_per_sh));
-    if (v.dtype == kF16) hipLaunchKernelGGL((fp8_prefill_kernel<kF16>), grid, dim3(kF8Threads), 0, st, a);
-    else hipLaunchKernelGGL((fp8_prefill_kernel<kBF16>), grid, dim3(kF8Threads), 0, st, a);
     return (int)hipGetLastError();
 }
 

@@ -25,6 +25,12 @@
 // Tiles that reach the residual, the end of the sequence or (second reading
 // below) the chunk are restored from the right source per token.
 //
+// The FP8 cache ("4.4 KV Cache 量化", section 4) runs the same kernel with
+// BITS = 8: each tile's E4M3 bytes become exact fp16 values (value times 2^-8)
+// in one conversion per pair, so the Keys need no lo part (32 products per
+// tile instead of 48); the Key scale folds into the softmax scale, the Value
+// scale multiplies the normalised output, and there is no residual.
+//
 // Second reading of the prefill (the pages leave it open): with a chunk given
 // at full precision, the call comes before the chunk is stored; seq_lens are
 // the lengths P before it, the chunk's rows sit at positions P .. P + n_q - 1,
@@ -81,6 +87,9 @@ struct PrefillArgs {
     int causal;
     int max_q_len;     // the caller's bound of every query span
     int wg_per_sh;     // work groups per (sequence, KV head)
+    const float* k_scale;  // FP8 cache: per-tensor or per-KV-head scales
+    const float* v_scale;
+    int per_head;
     uint16_t* out;
 };
 
@@ -97,6 +106,13 @@ __device__ __forceinline__ h2 code_pair(uint32_t x, int sh) {
     return __builtin_bit_cast(h2, m) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
 }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+// fp16 pair (value 2^-8) of E4M3 bytes 0, 1 of w, or of bytes 2, 3 (kHigh):
+// one gfx950 v_cvt_scalef32_pk_f16_fp8; the scale acts as a power of two, so
+// the pair is exact
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 0.00390625f, kHigh));
+}
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
 // The codes a thread restores for one tile: half of its Key slot and of its
@@ -132,11 +148,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int q0 = a.cu_q[s];
     const int nq = a.cu_q[s + 1] - q0;
     int P = a.seq_lens[s];  // tokens in the cache (before the chunk when it comes raw)
-    const int slot = a.slot_ids[s];
+    constexpr bool kF8 = BITS == 8;  // FP8 cache: no slots, no residual, no Key metadata
+    const int slot = kF8 ? 0 : a.slot_ids[s];
     const bool bad = slot < 0 || slot >= V.max_seqs || P < 0;
     const bool raw_chunk = a.k_chunk != nullptr;
     if (wg == 0 && wave == 0) {  // device-side errors of this sequence, reported once
-        uint32_t e = (slot < 0 || slot >= V.max_seqs ? KIVI_DEVERR_SLOT : 0u) | (P < 0 ? KIVI_DEVERR_LENGTH : 0u);
+        uint32_t e = (!kF8 && (slot < 0 || slot >= V.max_seqs) ? KIVI_DEVERR_SLOT : 0u) |
+                     (P < 0 ? KIVI_DEVERR_LENGTH : 0u);
         if (nq < 0 || nq > a.max_q_len || (!raw_chunk && !bad && nq > P)) e |= KIVI_DEVERR_QUERY;
         if (!bad && (long long)P + (raw_chunk ? max(nq, 0) : 0) > (long long)a.bt_stride * V.Bk)
             e |= KIVI_DEVERR_LENGTH;
@@ -148,7 +166,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int row0_wg = wg * kRowsWg;
     if (row0_wg >= nrows) return;  // no rows for this work group (uniform)
     const int R = V.R;
-    const int TK = R * (P / R), TV = value_boundary(V, P);  // quantised in the cache
+    // quantised in the cache (the whole sequence in an FP8 cache)
+    const int TK = kF8 ? P : R * (P / R), TV = kF8 ? P : value_boundary(V, P);
 
     // ---- this lane's row: column l % 32 of the wave's 32 rows ----
     const int half = lane >> 5, col = lane & 31;
@@ -175,10 +194,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int n_tiles = wg_max >= 0 ? (wg_max + kTileTok) / kTileTok : 0;
 
     // ---- query operand: lane (col, half) holds q[row][16 ks + 8 half .. + 7] ----
-    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // scores kept as sgn q.k
+    // FP8: Keys enter as value * 2^-8, so the Key scale times 2^8 joins the softmax scale
+    const float xs = kF8 ? a.scale_log2 * a.k_scale[a.per_head ? h : 0] * 256.0f : a.scale_log2;
+    const float sgn = xs < 0.0f ? -1.0f : 1.0f;  // scores kept as sgn q.k
     // weight 2^(x - m), x = score * c2; a zero scale (uniform weights) is
     // taken as the smallest normal one, so that -inf * c2 stays -inf
-    const float c2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+    const float c2 = fmaxf(fabsf(xs), 1.17549435e-38f);
     h8 Qb[8];
     {
         const uint16_t* qrow = a.q + ((size_t)(q0 + qi) * HQ + h * g + qh) * kHeadDim + 8 * half;
@@ -210,12 +231,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int u = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // per wave
     const int L = lane, m = L & 15, j = L >> 4;
     const int32_t* bt = a.block_table + (size_t)s * a.bt_stride;
-    const uint16_t* ringK = V.k_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
-    const uint16_t* ringV = V.v_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
+    const uint16_t* ringK = kF8 ? nullptr : V.k_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
+    const uint16_t* ringV = kF8 ? nullptr : V.v_ring + ((size_t)max(slot, 0) * H + h) * V.ring_elems;
     // Pages per Key group (G / Bk) and the Key channels whose metadata one
     // page holds (128 Bk / G) are powers of two: G / Bk divides 128. Bk is a
     // multiple of 16, usually a power of two as well.
-    const int gpb_lg = __builtin_ctz((unsigned)(V.G / V.Bk));
+    const int gpb_lg = kF8 ? 0 : __builtin_ctz((unsigned)(V.G / V.Bk));
     const int nch_lg = __builtin_ctz((unsigned)kHeadDim) - gpb_lg, nch = 1 << nch_lg;
     const bool bk_pow2 = (V.Bk & (V.Bk - 1)) == 0;
     const int bk_lg = __builtin_ctz((unsigned)V.Bk);
@@ -237,6 +258,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     _Float16* const meta_lds = lds + 2 * kStageHalfs;
     auto issue_meta = [&](int k, uint32_t& ms, uint32_t& mz) {
         ms = mz = 0;
+        if constexpr (kF8) return;
         const int p_sub = kTileTok * k + 16 * u;
         if (pt == 0 && k < n_tiles && p_sub < TK) {
             // group jg = p_sub / G; channel ch's pair sits on page jg G / Bk + ch / nch
@@ -250,7 +272,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
     };
     auto store_meta = [&](int k, uint32_t ms, uint32_t mz) {
-        if (pt != 0) return;
+        if (kF8 || pt != 0) return;
         _Float16* mt = meta_lds + (k & 1) * kMetaHalfs + u * 2 * kHeadDim;
         *reinterpret_cast<uint32_t*>(mt + 2 * L) = ms;
         *reinterpret_cast<uint32_t*>(mt + kHeadDim + 2 * L) = mz;
@@ -262,7 +284,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto load_slot_k = [&](int blk, int p_sub, SlotRegs<BITS, NGP>& x) {
         const uint8_t* base = V.k_codes + ((size_t)blk * H + h) * V.code_bytes +
                               (mod_bk(p_sub) / kTile) * TILE_BYTES + SLOT_BYTES * L + 4 * KW * pt;
-        if constexpr (KW == 2) {
+        if constexpr (KW == 4) {
+            const uint4 w = *reinterpret_cast<const uint4*>(base);
+            x.k[0] = w.x; x.k[1] = w.y; x.k[2] = w.z; x.k[3] = w.w;
+        } else if constexpr (KW == 2) {
             const uint2 w = *reinterpret_cast<const uint2*>(base);
             x.k[0] = w.x; x.k[1] = w.y;
         } else {
@@ -272,7 +297,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto load_slot_v = [&](int blk, int p_sub, SlotRegs<BITS, NGP>& x) {
         const uint8_t* base = V.v_codes + ((size_t)blk * H + h) * V.code_bytes +
                               (mod_bk(p_sub) / kTile) * TILE_BYTES + SLOT_BYTES * L + 4 * KW * pt;
-        if constexpr (KW == 2) {
+        if constexpr (KW == 4) {
+            const uint4 w = *reinterpret_cast<const uint4*>(base);
+            x.v[0] = w.x; x.v[1] = w.y; x.v[2] = w.z; x.v[3] = w.w;
+            return;  // no Value metadata in an FP8 cache
+        } else if constexpr (KW == 2) {
             const uint2 w = *reinterpret_cast<const uint2*>(base);
             x.v[0] = w.x; x.v[1] = w.y;
         } else {
@@ -308,6 +337,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     // precision (the product is exact), and t - hi is exact before its
     // rounding to fp16
     auto store_k_codes = [&](_Float16* st, int k, const uint32_t* kw) {
+        if constexpr (kF8) {  // exact values: no lo part (the products skip it)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int off = (16 * u + m) * kKRow + 32 * (2 * pt + rr) + 8 * j;
+                *reinterpret_cast<uint4*>(st + off) =
+                    (uint4){e4m3_pair<false>(kw[2 * rr]), e4m3_pair<true>(kw[2 * rr]),
+                            e4m3_pair<false>(kw[2 * rr + 1]), e4m3_pair<true>(kw[2 * rr + 1])};
+            }
+            return;
+        }
         const _Float16* mt = meta_lds + (k & 1) * kMetaHalfs + u * 2 * kHeadDim;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
@@ -360,8 +399,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto fill_pure = [&](_Float16* st, int k, const SlotRegs<BITS, NGP>& x) {
         store_k_codes(st, k, x.k);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            store_v(st, 4 * pt + tt, as_u32(v_from_codes(x, tt, 0)), as_u32(v_from_codes(x, tt, 1)));
+        for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (kF8)  // byte r of the word: token 4j + r of channel 16 (4 pt + tt) + m
+                store_v(st, 4 * pt + tt, e4m3_pair<false>(x.v[tt]), e4m3_pair<true>(x.v[tt]));
+            else
+                store_v(st, 4 * pt + tt, as_u32(v_from_codes(x, tt, 0)), as_u32(v_from_codes(x, tt, 1)));
+        }
     };
     // Any tile: per sub-tile (Keys; TK is a multiple of 16) and per token
     // (Values) from codes, the residual ring, the raw chunk, or zeros past the
@@ -369,6 +412,30 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto fill_any = [&](_Float16* st, int k) {
         const int t0 = kTileTok * k;
         const int p_sub = t0 + 16 * u;
+        if constexpr (kF8) {
+            // bytes of tokens at or past T were never written and may hold an
+            // E4M3 NaN (0 times NaN is NaN): they become zeros
+            const int blk = p_sub < T ? page_of(p_sub) : -1;
+            SlotRegs<BITS, NGP> x;
+#pragma unroll
+            for (int q = 0; q < KW; ++q) x.k[q] = x.v[q] = 0;
+            if (blk >= 0) {
+                load_slot_k(blk, p_sub, x);
+                load_slot_v(blk, p_sub, x);
+            }
+            if (p_sub + m >= T) {
+#pragma unroll
+                for (int q = 0; q < KW; ++q) x.k[q] = 0;
+            }
+            uint32_t keep = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (p_sub + 4 * j + r < T) keep |= 0xFFu << (8 * r);
+#pragma unroll
+            for (int q = 0; q < KW; ++q) x.v[q] &= keep;
+            fill_pure(st, k, x);
+            return;
+        }
         const int blk = (p_sub < TV || p_sub < TK) ? page_of(p_sub) : -1;
         SlotRegs<BITS, NGP> x;
 #pragma unroll
@@ -447,6 +514,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         if (blk < 0) {  // no page: its slot restores to zero values
 #pragma unroll
             for (int q = 0; q < 4 * NGP; ++q) x.vm[q] = 0;
+            if constexpr (kF8) {
+#pragma unroll
+                for (int q = 0; q < KW; ++q) x.k[q] = x.v[q] = 0;
+            }
         }
     };
 
@@ -514,8 +585,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             const h8 b1 = *reinterpret_cast<const h8*>(st + kKHalfs + o1);
             S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, Qb[ks], S0, 0, 0, 0);
             S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, Qb[ks], S1, 0, 0, 0);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[ks], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[ks], S1, 0, 0, 0);
+            if constexpr (!kF8) {  // FP8 Keys are exact in fp16
+                S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[ks], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[ks], S1, 0, 0, 0);
+            }
         }
         // block 0's softmax and PV while block 1's scores are on the matrix cores
         const _Float16* vst = st + kVOff;
@@ -594,7 +667,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         l_acc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
     if (!(row < nrows)) return;
-    const float inv = l_acc > 0.0f ? 1.0f / l_acc : 0.0f;
+    // FP8: the Values entered as value * 2^-8
+    const float vsc = kF8 ? a.v_scale[a.per_head ? h : 0] * 256.0f : 1.0f;
+    const float inv = l_acc > 0.0f ? vsc / l_acc : 0.0f;
     uint16_t* orow = a.out + ((size_t)(q0 + qi) * HQ + h * g + qh) * kHeadDim;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -612,11 +687,15 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 template <int BITS, int DT>
 void launch_pf(const PrefillArgs& a, int ng, dim3 grid, hipStream_t st) {
     dim3 block(kPThreads);
-    switch (ng) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 1>), grid, block, kPrefillLds, st, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 2>), grid, block, kPrefillLds, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 4>), grid, block, kPrefillLds, st, a); break;
-        default: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 8>), grid, block, kPrefillLds, st, a); break;
+    if constexpr (BITS == 8) {  // no Value groups in an FP8 cache
+        hipLaunchKernelGGL((prefill_kernel<8, DT, 1>), grid, block, kPrefillLds, st, a);
+    } else {
+        switch (ng) {
+            case 1: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 1>), grid, block, kPrefillLds, st, a); break;
+            case 2: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 2>), grid, block, kPrefillLds, st, a); break;
+            case 4: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 4>), grid, block, kPrefillLds, st, a); break;
+            default: hipLaunchKernelGGL((prefill_kernel<BITS, DT, 8>), grid, block, kPrefillLds, st, a); break;
+        }
     }
 }
 
@@ -655,6 +734,38 @@ int launch_prefill(const CacheView& v, int num_seqs, int num_q_heads, const void
         if (v.dtype == kF16) launch_pf<2, kF16>(a, ng, grid, st);
         else launch_pf<2, kBF16>(a, ng, grid, st);
     }
+    return (int)hipGetLastError();
+}
+
+int launch_fp8_prefill(const CacheView& v, int per_head, int num_seqs, int num_q_heads, const void* q,
+                       const int32_t* cu_q, int max_q_len, const int32_t* seq_lens, const float* k_scale,
+                       const float* v_scale, const int32_t* block_table, int bt_stride, float softmax_scale,
+                       int causal, void* out, void* stream) {
+    PrefillArgs a{};
+    a.v = v;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_chunk = nullptr;
+    a.v_chunk = nullptr;
+    a.cu_q = cu_q;
+    a.slot_ids = nullptr;  // an FP8 cache has no residual slots
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.num_q_heads = num_q_heads;
+    a.gqa = num_q_heads / v.H;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.causal = causal;
+    a.max_q_len = max_q_len;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.per_head = per_head;
+    const long long rows = (long long)max_q_len * a.gqa;
+    a.wg_per_sh = (int)((rows + kRowsWg - 1) / kRowsWg);
+    a.out = static_cast<uint16_t*>(out);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    dim3 grid((unsigned)((size_t)num_seqs * v.H * a.wg_per_sh));
+    if (v.dtype == kF16) launch_pf<8, kF16>(a, 1, grid, st);
+    else launch_pf<8, kBF16>(a, 1, grid, st);
     return (int)hipGetLastError();
 }
 
