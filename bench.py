@@ -618,7 +618,7 @@ def fp8_prefill_leg(torch, kivi, inputs, dev, n_iter: int, check: bool):
            "flop_per_launch": flop,
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "kernel": "fp8_prefill_kernel, one kivi_fp8_prefill_attention call"}}
+                        "kernel": "prefill_kernel<8, 1, 1> (the FP8 instance), one kivi_fp8_prefill_attention call"}}
     if check:
         import oracle
         torch.cuda.synchronize()
