@@ -48,8 +48,9 @@ constexpr int kThreads = 512;
 constexpr int kBtPre = 1024;  // page-table entries a work group can hold in LDS
 constexpr int kWaves = 8;
 // Main tiles of a SIMD's older wave, in percent of an even split (the
-// younger wave takes 200 minus this): measured best at 130 on MI355X.
-constexpr int kOldShare = 130;
+// younger wave takes 200 minus this): measured best at 110 on MI355X with
+// 4-tile blocks (130 with 2-tile buffers); an even split is slowest.
+constexpr int kOldShare = 110;
 constexpr int kAppendShare = 70;  // main-tile share of the appending wave (20-70 measure alike)
 // Main-tile weight of each of the two Key-flush waves on a step that flushes
 // (an even share is 300; their share goes to waves 0-3): the flush keeps them
@@ -300,7 +301,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         const int sp = ws / kWaves, wv = ws % kWaves;
         long long before = (long long)sp * kWaves * 300;
         for (int w = 0; w < wv; ++w) before += weight(w);
-        return (int)((before * c.n_main) / ((long long)nslots * 300));
+        const int t = (int)((before * c.n_main) / ((long long)nslots * 300));
+        if constexpr (kHalf == 4) {  // 4-tile blocks: ranges start on block boundaries
+            if (ws >= nslots) return c.n_main;
+            return min(c.n_main, (t + 2) & ~3);
+        }
+        return t;
     };
     const int wslot = split * kWaves + wave;
     const int m_begin = slot_start(wslot);
