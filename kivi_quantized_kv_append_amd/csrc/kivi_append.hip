@@ -1,8 +1,9 @@
 // Append kernel: one work group of 256 threads per (sequence, KV head), or
-// gridDim.y parts of one for the quantisation of a bulk append (a prefill
-// chunk): Key groups and Value token quads are dealt round-robin, every unit
-// writes disjoint code words and metadata, and phase B then runs as a second
-// launch on the same stream, after every part has read the ring. The work of
+// gridDim.y parts of one for a bulk append (a prefill chunk): Key groups and
+// Value token quads are dealt round-robin, every unit writes disjoint code
+// words and metadata, and phase B (the new residual rows, dealt round-robin
+// over the same parts) then runs as a second launch on the same stream, after
+// every part has read the ring. The work of
 // one (sequence, head) is append_body (kivi_append_body.h).
 
 #include "kivi_append_body.h"
@@ -64,7 +65,7 @@ int launch_append(const CacheView& v, int num_seqs, const int32_t* slot_ids,
         launch(0, 1);
     } else {
         launch(1, parts);
-        launch(2, 1);
+        launch(2, parts);
     }
     return (int)hipGetLastError();
 }

@@ -136,6 +136,8 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
             const int base = j * G;
             const int lo = half * (G / NQ), hi = lo + G / NQ;
             float mn = INFINITY, mx = -INFINITY;
+            // unrolled so that several tokens' loads are in flight at once
+#pragma unroll 8
             for (int i = lo; i < hi; ++i) {
                 float x = kval(base + i, c);
                 mn = fminf(mn, x);
@@ -167,6 +169,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
             __syncthreads();
             {
                 const float S = sm_S[c], Z = sm_Z[c];
+#pragma unroll 8
                 for (int i = lo; i < hi; ++i)
                     sm_codes[i * kHeadDim + c] = (uint8_t)group_code(kval(base + i, c), S, Z, QMAX);
             }
@@ -306,15 +309,33 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int s, int h, i
             if (nv > 0 && tid < kHeadDim) ringV[vring_index(R, T0, tid)] = row_v;
             return;
         }
+        // Phase B is split over the parts like phase A (mode 2 with nparts
+        // parts; mode 0 is a single part). Loops are unrolled so that several
+        // loads are in flight per thread.
+        const int tq = tid + NT * part, step = NT * nparts;
         // Key ring: token-major rows, 16-byte chunks
-        for (int q = tid; q < nk * 16; q += NT) {
+#pragma unroll 4
+        for (int q = tq; q < nk * 16; q += step) {
             const int p = k_first + q / 16, ch = (q % 16) * 8;
             const uint4 val = *reinterpret_cast<const uint4*>(inK + (size_t)(p - T0) * in_stride + ch);
             *reinterpret_cast<uint4*>(ringK + (size_t)(p % R) * kHeadDim + ch) = val;
         }
-        // Value ring: quads of [128 channels][4 tokens]
-        for (int q = tid; q < nv * kHeadDim; q += NT) {
+        // Value ring: quads of [128 channels][4 tokens]; a quad that the new
+        // rows fill whole is one 8-byte store per channel, the (at most two)
+        // partial quads at the ends take single elements
+        const int qa = (v_first + 3) / 4, qb = T1 / 4;  // whole quads [4 qa, 4 qb)
+        if (qb > qa) {
+#pragma unroll 4
+            for (int q = tq; q < (qb - qa) * kHeadDim; q += step) {
+                const int p0 = 4 * (qa + q / kHeadDim), ch = q % kHeadDim;
+                const uint16_t* src = inV + (size_t)(p0 - T0) * in_stride + ch;
+                const uint32_t v0 = src[0], v1 = src[in_stride], v2 = src[2 * in_stride], v3 = src[3 * in_stride];
+                *reinterpret_cast<uint2*>(ringV + vring_index(R, p0, ch)) = (uint2){v0 | (v1 << 16), v2 | (v3 << 16)};
+            }
+        }
+        for (int q = tq; q < nv * kHeadDim; q += step) {
             const int p = v_first + q / kHeadDim, ch = q % kHeadDim;
+            if (qb > qa && p >= 4 * qa && p < 4 * qb) continue;  // written as a whole quad
             ringV[vring_index(R, p, ch)] = inV[(size_t)(p - T0) * in_stride + ch];
         }
     }
