@@ -325,7 +325,9 @@ class GpuCache:
             self.lens[s] += n
         return dk, dv
 
-    def decode(self, q_bits: np.ndarray, scale: float, seqs=None, max_seq_len=None):
+    def decode(self, q_bits: np.ndarray, scale: float, seqs=None, max_seq_len=None, ws=None):
+        """Decode attention through kivi_decode_attention; `ws`: a workspace to use (a
+        uint8 device tensor, at least the size asked for), else a fresh zeroed one."""
         torch = self.torch
         seqs = list(range(self.w.num_seqs)) if seqs is None else list(seqs)
         HQ = self.w.num_q_heads
@@ -333,7 +335,9 @@ class GpuCache:
         out = torch.zeros((len(seqs), HQ, D), dtype=torch.int16, device=self.device)
         msl = int(self.lens[seqs].max()) if max_seq_len is None else max_seq_len
         ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, len(seqs), HQ, msl)
-        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        if ws is None:
+            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        assert ws.numel() >= ws_bytes
         bt = self.t(self.bt_np[seqs])
         kivi.kivi_decode_attention(self.handle, len(seqs), HQ, q, self.t(np.asarray(seqs, np.int32)),
                                    self.t(self.lens[seqs].astype(np.int32)), msl, bt, bt.shape[1],
@@ -517,11 +521,13 @@ class Fp8GpuCache:
         self.lens += np.asarray(ns)
         torch.cuda.synchronize()
 
-    def decode(self, q_bits: np.ndarray, scale: float) -> np.ndarray:
+    def decode(self, q_bits: np.ndarray, scale: float, ws=None) -> np.ndarray:
         torch, S, HQ = self.torch, self.w.num_seqs, self.w.num_q_heads
         msl = int(self.lens.max())
         ws_bytes = kivi.kivi_decode_workspace_bytes(self.handle, S, HQ, msl)
-        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        if ws is None:
+            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        assert ws.numel() >= ws_bytes
         out = torch.zeros((S, HQ, D), dtype=torch.int16, device=self.device)
         kivi.kivi_fp8_decode_attention(self.handle, S, HQ, self.t(np.ascontiguousarray(q_bits).view(np.int16)),
                                        self.t(self.lens.astype(np.int32)), msl, self.ks, self.vs, self.bt,
