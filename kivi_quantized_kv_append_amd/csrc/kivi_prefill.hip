@@ -14,11 +14,12 @@
 // outlier channels reach |k| of tens, where one fp16 rounding alone moves a
 // score by more than the attention tolerance allows. Values are restored to
 // fp16 with one packed FMA per pair (their rounding is averaged out).
-// Two LDS stages: the next tile's codes and metadata are loaded before the
-// current tile is computed and restored after it, one barrier per tile.
+// Two LDS stages: the next tile is restored while the current tile's score
+// products run, from codes loaded half a tile earlier; one barrier per tile.
 // Per wave and tile, on matrix cores (v_mfma_f32_32x32x16_f16, fp32 sums):
 //   S^T[64 tokens][32 rows] = (K_hi + K_lo)[64][128] Q^T[128][32]   32 MFMAs
-//   online softmax per row (one lane pair per row), weights as fp16
+//   online softmax per row (one lane pair per row; the running max moves
+//   per tile), weights as fp16
 //   O^T[128][32] += V^T[128][64] P^T[64][32]                        16 MFMAs
 // The k-order of the P^T V MFMAs is the order in which the score MFMAs leave
 // the weights in the lanes; the Value rows in LDS are stored in that order.
@@ -527,29 +528,137 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int cb = 0; cb < 4; ++cb) O[cb] = (f16v){};
     float m_run = -INFINITY, l_acc = 0.0f;
 
-    // Online softmax of one 32-token block of scores (lane: row col, tokens
-    // tb0 + 8 (v / 4) + 4 half + v % 4): the block's maximum moves the running
-    // maximum (in log2 units) only when it passes it by kLazy; the weights
-    // 2^(score c2 - m) go to two fp16 B operands (k-steps 2 b, 2 b + 1),
-    // rounded to nearest.
-    // Scores of tokens past the row's last become -inf, only on blocks some
-    // row of the wave does not see whole (c2 > 0, so their weights are 0).
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    auto softmax_block = [&](f16v& S, int tb0, h8* Pb) {
-        if (tb0 + 31 > wave_min) {  // uniform
-            const int lim = my_last - tb0 - 4 * half;  // the row sees v with 8 (v / 4) + v % 4 <= lim
+    // ---- per tile and wave (the lane holds row col; tokens
+    // t0 + 32 b + 8 (v / 4) + 4 half + v % 4 of block b) ----
+    // Scores S^T[token][row] of the tile's two 32-token blocks, Keys as hi + lo
+    // (the two blocks' accumulations alternate, so that no product waits for
+    // the one before it).
+    auto qk = [&](const _Float16* st, f16v& S0, f16v& S1) {
+        S0 = (f16v){};
+        S1 = (f16v){};
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                if (8 * (v >> 2) + (v & 3) > lim) S[v] = -INFINITY;
+        for (int ks = 0; ks < 8; ++ks) {
+            const int o0 = col * kKRow + 16 * ks + 8 * half, o1 = o0 + 32 * kKRow;
+            const h8 a0 = *reinterpret_cast<const h8*>(st + o0), a1 = *reinterpret_cast<const h8*>(st + o1);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, Qb[ks], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, Qb[ks], S1, 0, 0, 0);
+            if constexpr (!kF8) {  // FP8 Keys are exact in fp16
+                const h8 b0 = *reinterpret_cast<const h8*>(st + kKHalfs + o0);
+                const h8 b1 = *reinterpret_cast<const h8*>(st + kKHalfs + o1);
+                S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[ks], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[ks], S1, 0, 0, 0);
+            }
         }
-        float mx = S[0];
+    };
+    // Tile k's scores (from stage cur) interleaved with the restore of pure
+    // tile k + 1 into stage nxt: 8 steps, one per 16-channel k-step of the
+    // products; step i issues the k-step's 4 products (operands read one step
+    // ahead), restores pair e = i % 4 of Key channel run 2 pt + i / 4 and
+    // Value pair i % 2 of channel tile 4 pt + i / 2, and ends at a scheduling
+    // barrier, so that the products and the vector work stay mixed.
+    auto qk_fill = [&](const _Float16* st, f16v& S0, f16v& S1, _Float16* nst, int kn,
+                       const SlotRegs<BITS, NGP>& x) {
+        S0 = (f16v){};
+        S1 = (f16v){};
+        const _Float16* mt = meta_lds + (kn & 1) * kMetaHalfs + u * 2 * kHeadDim;
+        uint32_t sw[2][4], zw[2][4];
+        if constexpr (!kF8) {
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+            for (int rr = 0; rr < 2; ++rr) {
+                const uint4 sv = *reinterpret_cast<const uint4*>(mt + 32 * (2 * pt + rr) + 8 * j);
+                const uint4 zv = *reinterpret_cast<const uint4*>(mt + kHeadDim + 32 * (2 * pt + rr) + 8 * j);
+                sw[rr][0] = sv.x; sw[rr][1] = sv.y; sw[rr][2] = sv.z; sw[rr][3] = sv.w;
+                zw[rr][0] = zv.x; zw[rr][1] = zv.y; zw[rr][2] = zv.z; zw[rr][3] = zv.w;
+            }
+        }
+        auto operands = [&](int ks, h8& a0, h8& a1, h8& b0, h8& b1) {
+            const int o0 = col * kKRow + 16 * ks + 8 * half, o1 = o0 + 32 * kKRow;
+            a0 = *reinterpret_cast<const h8*>(st + o0);
+            a1 = *reinterpret_cast<const h8*>(st + o1);
+            if constexpr (!kF8) {
+                b0 = *reinterpret_cast<const h8*>(st + kKHalfs + o0);
+                b1 = *reinterpret_cast<const h8*>(st + kKHalfs + o1);
+            }
+        };
+        h8 A0, A1, B0, B1;
+        operands(0, A0, A1, B0, B1);
+        uint32_t hw[4], lw[4], vv[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const h8 a0 = A0, a1 = A1, b0 = B0, b1 = B1;
+            if (i < 7) operands(i + 1, A0, A1, B0, B1);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, Qb[i], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, Qb[i], S1, 0, 0, 0);
+            if constexpr (!kF8) {
+                S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[i], S0, 0, 0, 0);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[i], S1, 0, 0, 0);
+            }
+            // Keys: pair e of channel run r (as store_k_codes)
+            const int rr = i >> 2, e = i & 3, r = 2 * pt + rr;
+            if constexpr (kF8) {
+                if (e == 3) {
+                    const int off = (16 * u + m) * kKRow + 32 * r + 8 * j;
+                    *reinterpret_cast<uint4*>(nst + off) =
+                        (uint4){e4m3_pair<false>(x.k[2 * rr]), e4m3_pair<true>(x.k[2 * rr]),
+                                e4m3_pair<false>(x.k[2 * rr + 1]), e4m3_pair<true>(x.k[2 * rr + 1])};
+                }
+            } else {
+                h2 c;
+                if constexpr (BITS == 4) c = code_pair<4>(x.k[rr], 4 * e);
+                else c = code_pair<2>(x.k[0], 2 * (e + 4 * rr));
+                const h2 sc = as_h2(sw[rr][e]), zc = as_h2(zw[rr][e]);
+                const h2 hi = __builtin_elementwise_fma(c, sc, zc);
+                h2 lo;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float t = __builtin_fmaf((float)c[q], (float)sc[q], (float)zc[q]);
+                    lo[q] = (_Float16)__builtin_fmaf((float)hi[q], -1.0f, t);
+                }
+                hw[e] = as_u32(hi);
+                lw[e] = as_u32(lo);
+                if (e == 3) {
+                    const int off = (16 * u + m) * kKRow + 32 * r + 8 * j;
+                    *reinterpret_cast<uint4*>(nst + off) = (uint4){hw[0], hw[1], hw[2], hw[3]};
+                    *reinterpret_cast<uint4*>(nst + kKHalfs + off) = (uint4){lw[0], lw[1], lw[2], lw[3]};
+                }
+            }
+            // Values: pair i % 2 of channel tile 4 pt + i / 2
+            const int tt = i >> 1, kv = i & 1;
+            if constexpr (kF8) {
+                if (kv == 1) store_v(nst, 4 * pt + tt, e4m3_pair<false>(x.v[tt]), e4m3_pair<true>(x.v[tt]));
+            } else {
+                vv[kv] = as_u32(v_from_codes(x, tt, kv));
+                if (kv == 1) store_v(nst, 4 * pt + tt, vv[0], vv[1]);
+            }
+#pragma unroll
+            for (int q = 0; q < (kF8 ? 2 : 4); ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kF8 ? 2 : 4, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Online softmax, per tile: scores of tokens past the row's last become
+    // -inf (only on tiles some row of the wave does not see whole; c2 > 0, so
+    // their weights are 0); the tile's maximum (log2 units) moves the running
+    // maximum only when it passes it by kLazy.
+    auto tile_max = [&](f16v& S0, f16v& S1, int t0) {
+        if (t0 + kTileTok - 1 > wave_min) {  // uniform
+            const int lim = my_last - t0 - 4 * half;  // the row sees v with 8 (v / 4) + v % 4 <= lim
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (8 * (v >> 2) + (v & 3) > lim) S0[v] = -INFINITY;
+                if (32 + 8 * (v >> 2) + (v & 3) > lim) S1[v] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(S0[v], S1[v]));
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        const float mxl = mx * c2;  // -inf when the row sees none of the block
+        const float mxl = mx * c2;  // -inf when the row sees none of the tile
         if (__builtin_amdgcn_ballot_w64(mxl > m_run + kLazy) != 0) {  // rare: move the running max
             const float mnew = fmaxf(m_run, mxl);
             const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mnew);
@@ -558,6 +667,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
             for (int cb = 0; cb < 4; ++cb) O[cb] *= f;
             m_run = mnew;
         }
+    };
+    // Weights 2^(score c2 - m) of one block into two fp16 B operands (k-steps
+    // 2 b, 2 b + 1), rounded to nearest; their sum joins l.
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    auto weights = [&](const f16v& S, h8* Pb) {
         const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -572,59 +686,32 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
                 Pb[kk][2 * e + 1] = pp[1];
             }
     };
-    auto compute = [&](const _Float16* st, int t0) {
-        // S^T[token][row] for the tile's two 32-token blocks, Keys as hi + lo
-        // (the two blocks' accumulations alternate, so that no product waits
-        // for the one before it)
-        f16v S0 = (f16v){}, S1 = (f16v){};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int o0 = col * kKRow + 16 * ks + 8 * half, o1 = o0 + 32 * kKRow;
-            const h8 a0 = *reinterpret_cast<const h8*>(st + o0), a1 = *reinterpret_cast<const h8*>(st + o1);
-            const h8 b0 = *reinterpret_cast<const h8*>(st + kKHalfs + o0);
-            const h8 b1 = *reinterpret_cast<const h8*>(st + kKHalfs + o1);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, Qb[ks], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, Qb[ks], S1, 0, 0, 0);
-            if constexpr (!kF8) {  // FP8 Keys are exact in fp16
-                S0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, Qb[ks], S0, 0, 0, 0);
-                S1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, Qb[ks], S1, 0, 0, 0);
-            }
-        }
-        // block 0's softmax and PV while block 1's scores are on the matrix cores
-        const _Float16* vst = st + kVOff;
-        h8 Pb[2];
-        softmax_block(S0, t0, Pb);
+    // O^T[128][32] += V^T[128][32 tokens of block b] P^T
+    auto pv = [&](const _Float16* vst, int b, const h8* Pb) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const h8 av = *reinterpret_cast<const h8*>(vst + (32 * cb + col) * kVRow + 16 * kk + 8 * half);
-                O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, Pb[kk], O[cb], 0, 0, 0);
-            }
-        softmax_block(S1, t0 + 32, Pb);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const h8 av = *reinterpret_cast<const h8*>(vst + (32 * cb + col) * kVRow + 16 * (2 + kk) + 8 * half);
+                const h8 av = *reinterpret_cast<const h8*>(vst + (32 * cb + col) * kVRow + 16 * (2 * b + kk) + 8 * half);
                 O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, Pb[kk], O[cb], 0, 0, 0);
             }
     };
 
     // ---- the tile loop: two LDS stages, one barrier per tile ----
-    // The two halves of the work group take the iteration in opposite orders,
-    // so that on each SIMD (which runs one wave of each) one wave's matrix
-    // work meets the other's vector work. Iteration k:
-    //   first half (pt 0): loads of tile k + 1's codes and tile k + 2's Key
-    //     metadata; tile k's computation; tile k + 1's restore; the metadata
-    //     store;
-    //   second half (pt 1): tile k + 1's restore from the codes loaded in the
-    //     iteration before; the loads of tile k + 2's codes; tile k's
-    //     computation;
-    // then a barrier. A tile that is not pure is restored after the
-    // computation by both halves.
+    // Vector work issued between a wave's own matrix products overlaps them;
+    // the matrix products of one wave and the vector work of the other wave on
+    // the same SIMD hardly do (measured on MI355X: 903 cycles for both against
+    // 527 + 408 apart; 553 against 527 for the same work interleaved in one
+    // wave). So every wave interleaves: iteration k
+    //   (1) tile k's score products with the restore of tile k + 1 (from codes
+    //       loaded in the iteration before), one block of straight-line code;
+    //   (2) the loads of tile k + 2's codes and Key metadata;
+    //   (3) the tile's maximum (and, rarely, a rescale);
+    //   (4) block 0's weights, block 0's P V products interleaved with block
+    //       1's weights, block 1's P V products;
+    // then the metadata store and a barrier. A tile that is not pure is
+    // restored after the computation.
     if (n_tiles > 0) {
-        const bool early = pt == 1;  // uniform
         SlotRegs<BITS, (NG == 1 ? 1 : NG / 2)> nx;
         uint32_t ms, mz;
         issue_meta(0, ms, mz);
@@ -638,24 +725,40 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         } else {
             fill_any(lds, 0);
         }
-        if (early && n_tiles > 1 && pure(1)) issue_pure(1, nx);
+        if (n_tiles > 1 && pure(1)) issue_pure(1, nx);
         __syncthreads();
         for (int k = 0; k < n_tiles; ++k) {
-            _Float16* cur = lds + (k & 1) * kStageHalfs;
+            const _Float16* cur = lds + (k & 1) * kStageHalfs;
             _Float16* nxt = lds + ((k + 1) & 1) * kStageHalfs;
             const bool more = k + 1 < n_tiles;
             const bool nxt_pure = more && pure(k + 1);
-            if (early) {
-                if (nxt_pure) fill_pure(nxt, k + 1, nx);
-                if (k + 2 < n_tiles && pure(k + 2)) issue_pure(k + 2, nx);
+            f16v S0, S1;
+            if (nxt_pure) {
+                qk_fill(cur, S0, S1, nxt, k + 1, nx);
             } else {
-                if (nxt_pure) issue_pure(k + 1, nx);
-                issue_meta(k + 2, ms, mz);
+                qk(cur, S0, S1);
             }
-            compute(cur, kTileTok * k);
-            if (!early && nxt_pure) fill_pure(nxt, k + 1, nx);
+            if (k + 2 < n_tiles && pure(k + 2)) issue_pure(k + 2, nx);
+            issue_meta(k + 2, ms, mz);
+            tile_max(S0, S1, kTileTok * k);
+            const _Float16* vst = cur + kVOff;
+            h8 P0[2], P1[2];
+            weights(S0, P0);
+            pv(vst, 0, P0);
+            weights(S1, P1);
+            pv(vst, 1, P1);
+            // block 0's weights with the Value reads; block 0's products with
+            // block 1's weights; block 1's products
+            __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
             if (more && !nxt_pure) fill_any(nxt, k + 1);
-            if (!early) store_meta(k + 2, ms, mz);
+            store_meta(k + 2, ms, mz);
             __syncthreads();
         }
     }
