@@ -253,9 +253,9 @@ __device__ __forceinline__ float max4(f4 x) { return max2(max2(x[0], x[1]), max2
 // kLazyLog2 / (|scale| log2 e): weights stay below 2^kLazyLog2 and the
 // rescale of the accumulators is rare.
 // O[t][r] holds O^T[16 t + 4 (lane >> 4) + r][head]; wsum[gg][vb] sums the
-// Value-side weights of channel group gg and pair-factor variant vb (int4
-// codes carry a 1024 offset, so each output channel holds 1024 wsum too
-// much until the merge takes it out).
+// Value-side weights of channel group gg and pair-factor variant vb (codes
+// that carry a 1024 offset leave each output channel 1024 wsum too much
+// until the merge takes it out).
 constexpr float kLazyLog2 = 2.0f;
 
 template <int NG, int NB>
@@ -297,14 +297,15 @@ struct Acc {
     __device__ __forceinline__ float weight(float x, float sl2) const {
         return __builtin_amdgcn_exp2f(__builtin_fmaf(x, sl2, mneg));
     }
-    // Take the int4 1024 offsets accumulated so far out of O. An accumulator
-    // that carries them is ~137 times larger than its useful part (code
-    // fields of 0..15 under 1024), so fp32 rounding in the MFMA sums grows
-    // with the tokens summed; flushing every few hundred tokens bounds it.
-    // Wave-uniform call.
+    // Take the 1024 offsets accumulated so far out of O (int4 codes, and int2
+    // codes in 4-tile blocks; elsewhere int2 codes enter exact and wsum stays
+    // 0). An accumulator that carries them is ~137 times larger than its
+    // useful part for int4 (fields of 0..15 under 1024), ~680 times for int2,
+    // so fp32 rounding in the MFMA sums grows with the tokens summed;
+    // flushing every few hundred tokens bounds it. Wave-uniform call.
     template <int BITS>
     __device__ __forceinline__ void flush_offsets() {
-        if constexpr (BITS == 4) {
+        {
             float c[NG][NB];
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg)

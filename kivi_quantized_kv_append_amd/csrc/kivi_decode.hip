@@ -767,16 +767,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                                              st.zacc[gg], false);
             st.zacc[gg] = __builtin_amdgcn_fdot2(pp23, __builtin_bit_cast(h2, __builtin_amdgcn_perm(m3, m2, 0x07060302u)),
                                                  z, false);
-            if constexpr (BITS == 4) {
-                st.wsum[gg][0] =
-                    __builtin_amdgcn_fdot2(w23, one, __builtin_amdgcn_fdot2(w01, one, st.wsum[gg][0], false), false);
-            }
+            // the Value codes enter as 1024 + field (int4 and int2 alike): the
+            // 1024 offsets come out later as 1024 times the weights' sum
+            st.wsum[gg][0] =
+                __builtin_amdgcn_fdot2(w23, one, __builtin_amdgcn_fdot2(w01, one, st.wsum[gg][0], false), false);
             Bq[gg][0][0] = diag(__builtin_bit_cast(uint32_t, w01));
             Bq[gg][0][1] = diag(__builtin_bit_cast(uint32_t, w23));
             if constexpr (NB == 2) {  // odd channel tiles: fields 4 places up (factor 1/16)
                 const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-                Bq[gg][NB - 1][0] = diag(__builtin_bit_cast(uint32_t, w01 * k16));
-                Bq[gg][NB - 1][1] = diag(__builtin_bit_cast(uint32_t, w23 * k16));
+                const h2 w01s = w01 * k16, w23s = w23 * k16;
+                st.wsum[gg][1] =
+                    __builtin_amdgcn_fdot2(w23s, one, __builtin_amdgcn_fdot2(w01s, one, st.wsum[gg][1], false), false);
+                Bq[gg][NB - 1][0] = diag(__builtin_bit_cast(uint32_t, w01s));
+                Bq[gg][NB - 1][1] = diag(__builtin_bit_cast(uint32_t, w23s));
             }
         }
         // PV: channel tile tt, k-step h: k = 8 jj + 2 e + q holds tile e's
@@ -793,8 +796,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                     a1[e] = magic_pair(ws, 0x00F000F0u);
                 } else {
                     const uint32_t x = b.v[e][tt >> 2], xs = (tt & 2) ? x >> 8 : x;
-                    a0[e] = exact_pair(xs, (tt & 1) ? 0x00300030u : 0x00030003u);
-                    a1[e] = exact_pair(xs, (tt & 1) ? 0x00C000C0u : 0x000C000Cu);
+                    a0[e] = magic_pair(xs, (tt & 1) ? 0x00300030u : 0x00030003u);
+                    a1[e] = magic_pair(xs, (tt & 1) ? 0x00C000C0u : 0x000C000Cu);
                 }
             }
             st.O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(make_h8(a0[0], a0[1], a0[2], a0[3]),
@@ -904,7 +907,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                     if (t0 + 4 >= m_end) break;
                     issue4(t0 + 8, qa);
                     compute4(qb, t0 + 4);
-                    if (++it == flush_period<kHalf>()) {
+                    // int2 fields are smaller against the 1024 offset: flush twice as often
+                    if (++it == (BITS == 2 ? flush_period<kHalf>() / 2 : flush_period<kHalf>())) {
                         it = 0;
                         st.template flush_offsets<BITS>();
                     }
@@ -952,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int gg = 0; gg < NG; ++gg) {
             const float z = xor_sum(st.zacc[gg]);
 #pragma unroll
-            for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - (BITS == 4 ? 1024.0f * xor_sum(st.wsum[gg][vb]) : 0.0f);
+            for (int vb = 0; vb < NB; ++vb) zt[gg][vb] = z - 1024.0f * xor_sum(st.wsum[gg][vb]);
         }
         __syncthreads();  // every wave is done with its LDS rows
         float* sm_m = reinterpret_cast<float*>(smem);  // [kWaves][g]
