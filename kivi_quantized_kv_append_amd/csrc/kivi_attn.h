@@ -136,10 +136,10 @@ __device__ __forceinline__ void unpack_v(const uint32_t* vw, h4 A[8]) {
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const uint32_t x = vw[w], x8 = x >> 8;
-            A[4 * w + 0] = make_h4(exact_pair(x, 0x00030003u), exact_pair(x, 0x000C000Cu));
-            A[4 * w + 1] = make_h4(exact_pair(x, 0x00300030u), exact_pair(x, 0x00C000C0u));
-            A[4 * w + 2] = make_h4(exact_pair(x8, 0x00030003u), exact_pair(x8, 0x000C000Cu));
-            A[4 * w + 3] = make_h4(exact_pair(x8, 0x00300030u), exact_pair(x8, 0x00C000C0u));
+            A[4 * w + 0] = make_h4(magic_pair(x, 0x00030003u), magic_pair(x, 0x000C000Cu));
+            A[4 * w + 1] = make_h4(magic_pair(x, 0x00300030u), magic_pair(x, 0x00C000C0u));
+            A[4 * w + 2] = make_h4(magic_pair(x8, 0x00030003u), magic_pair(x8, 0x000C000Cu));
+            A[4 * w + 3] = make_h4(magic_pair(x8, 0x00300030u), magic_pair(x8, 0x00C000C0u));
         }
     }
 }
@@ -297,10 +297,10 @@ struct Acc {
     __device__ __forceinline__ float weight(float x, float sl2) const {
         return __builtin_amdgcn_exp2f(__builtin_fmaf(x, sl2, mneg));
     }
-    // Take the 1024 offsets accumulated so far out of O (int4 codes, and int2
-    // codes in 4-tile blocks; elsewhere int2 codes enter exact and wsum stays
-    // 0). An accumulator that carries them is ~137 times larger than its
-    // useful part for int4 (fields of 0..15 under 1024), ~680 times for int2,
+    // Take the 1024 offsets accumulated so far out of O (main-range Value codes
+    // of int4 and int2 enter as 1024 + field). An accumulator that carries
+    // them is ~137 times larger than its useful part for int4 (fields of
+    // 0..15 under 1024), ~680 times for int2,
     // so fp32 rounding in the MFMA sums grows with the tokens summed;
     // flushing every few hundred tokens bounds it. Wave-uniform call.
     template <int BITS>
@@ -385,19 +385,23 @@ __device__ __forceinline__ void value_pair(Acc<NG, NB>& st, const uint32_t* vwa,
         Bw[gg][0][1] = __builtin_bit_cast(uint32_t, wa23);
         Bw[gg][0][2] = __builtin_bit_cast(uint32_t, wb01);
         Bw[gg][0][3] = __builtin_bit_cast(uint32_t, wb23);
-        if constexpr (BITS == 4) {
-            // the exact fp16 weights the MFMA multiplies the 1024 offsets with
-            float ws = __builtin_amdgcn_fdot2(wa01, one, st.wsum[gg][0], false);
-            ws = __builtin_amdgcn_fdot2(wa23, one, ws, false);
-            ws = __builtin_amdgcn_fdot2(wb01, one, ws, false);
-            st.wsum[gg][0] = __builtin_amdgcn_fdot2(wb23, one, ws, false);
-        } else {
+        // the exact fp16 weights the MFMA multiplies the 1024 offsets with
+        float ws = __builtin_amdgcn_fdot2(wa01, one, st.wsum[gg][0], false);
+        ws = __builtin_amdgcn_fdot2(wa23, one, ws, false);
+        ws = __builtin_amdgcn_fdot2(wb01, one, ws, false);
+        st.wsum[gg][0] = __builtin_amdgcn_fdot2(wb23, one, ws, false);
+        if constexpr (BITS == 2) {
             // odd channel tiles: fields 4 places up (factor 1/16)
             const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-            Bw[gg][1][0] = __builtin_bit_cast(uint32_t, wa01 * k16);
-            Bw[gg][1][1] = __builtin_bit_cast(uint32_t, wa23 * k16);
-            Bw[gg][1][2] = __builtin_bit_cast(uint32_t, wb01 * k16);
-            Bw[gg][1][3] = __builtin_bit_cast(uint32_t, wb23 * k16);
+            const h2 sa01 = wa01 * k16, sa23 = wa23 * k16, sb01 = wb01 * k16, sb23 = wb23 * k16;
+            Bw[gg][1][0] = __builtin_bit_cast(uint32_t, sa01);
+            Bw[gg][1][1] = __builtin_bit_cast(uint32_t, sa23);
+            Bw[gg][1][2] = __builtin_bit_cast(uint32_t, sb01);
+            Bw[gg][1][3] = __builtin_bit_cast(uint32_t, sb23);
+            float w1 = __builtin_amdgcn_fdot2(sa01, one, st.wsum[gg][1], false);
+            w1 = __builtin_amdgcn_fdot2(sa23, one, w1, false);
+            w1 = __builtin_amdgcn_fdot2(sb01, one, w1, false);
+            st.wsum[gg][1] = __builtin_amdgcn_fdot2(sb23, one, w1, false);
         }
         float z = st.zacc[gg];
 #pragma unroll

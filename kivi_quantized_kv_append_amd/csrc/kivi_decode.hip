@@ -927,7 +927,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             if (t0 + kHalf >= m_end) break;
             issue(t0 + 2 * kHalf, ba);
             compute(bb, t0 + kHalf);
-            if (++it == flush_period<kHalf>()) {
+            // int2 fields are smaller against the 1024 offset: flush twice as often
+            if (++it == (BITS == 2 ? (flush_period<kHalf>() + 1) / 2 : flush_period<kHalf>())) {
                 it = 0;
                 st.template flush_offsets<BITS>();
             }
