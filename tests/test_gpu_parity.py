@@ -248,3 +248,26 @@ def test_decode_two_heads_per_kv_head_wide_value_groups(bits):
     ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False,
                                threads=8)
     check_attention(got, ref, w.dtype, label=f"g 2, Gv 64, int{bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_two_tile_path_long_ranges(bits):
+    """The 2-tile path (7 query heads per KV head, 32-channel Value groups) with 256
+    (request, KV head) pairs, so no request is split and every wave streams a range of
+    ~30-60 tiles: the Value codes' 1024 offsets are taken out several times per range
+    (every 16 tiles). Every output against the oracle."""
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(3000, 7000, size=32)]
+    w = _variant(2, bits=bits, num_kv_heads=8, num_q_heads=56, v_group=32, num_seqs=32, seq_lens=lens,
+                 shuffle=True, pool_factor=1.1)
+    gc = GpuCache(w)
+    orc = oracle_caches(w)
+    rk, rv = zip(*w.kv_streams(8))
+    gc.append(list(rk), list(rv))
+    from kivi_quantized_kv_append_amd import kivi
+    assert kivi.kivi_decode_workspace_bytes(gc.handle, 32, 56, max(lens)) == 0  # no split
+    q = w.q_decode(5)
+    got = gc.decode(q, SCALE)
+    ref = oracle.attention_all(orc, w.num_q_heads, q, w.dtype, np.arange(w.num_seqs + 1), SCALE, False,
+                               threads=8)
+    check_attention(got, ref, w.dtype, label=f"2-tile path, g 7, Gv 32, int{bits}")
